@@ -1,0 +1,390 @@
+"""CPU oracle for the decode-time MoE layer with batch-aware expert selection.
+
+TEST INFRASTRUCTURE. Only the tests, the smoke check and the benchmark's CPU
+baseline may import this module. It shares no code with the HIP path (no
+kernels, headers, helpers, tables or pre/post-processing) and imports nothing
+from it. It is deliberately plain and slow: numpy, float64 arithmetic, each
+step written out in the order the pages describe.
+
+Sources (web pages on the subject; cited by title and section):
+  [Router]  "Router Caching and Optimization", section "Analyzing Router
+            Inference Cost": linear projection h = x W_g, softmax, top-k; and
+            the router-cache example, which ranks by softmax probability.
+  [OEA]     "Opportunistic Expert Activation: Batch-Aware Expert Routing for
+            Faster Decode Without Retraining", abstract and lay summary: each
+            token first keeps its most important experts, then piggybacks on
+            experts already loaded for other tokens of the batch.
+  [XShare]  "XShare: Collaborative in-Batch Expert Sharing for Faster MoE
+            Inference", summary and abstract: batch-aware selection as a
+            modular optimisation, maximising the total gating score of the
+            selected experts.
+  [Lynx]    "Lynx: Enabling Efficient MoE Inference through Dynamic
+            Batch-Aware Expert Selection", Technical Summary section 1
+            (latency follows the number of distinct experts the batch loads)
+            and section 2.2 (the batch activates a consolidated expert set).
+
+Readings where the pages are silent (each is stated where it is used):
+  R1  Per-token order: experts sorted by float32 logit descending, ties to
+      the lower expert index; -0.0 equals +0.0. Ranking by logit equals
+      ranking by probability (softmax is strictly increasing) and avoids
+      ties that rounding of exp would create.
+  R2  Decisions are taken on float32 values (the precision the kernels
+      compute in): logits are rounded to float32 before ranking and the
+      budget masses are rounded to float32 before ranking.
+  R3  Gate weights are the softmax restricted to the selected experts
+      (renormalised), for every policy, so oea(k0 = k) equals top-k.
+  R4  oea(k0): S = union over tokens of each token's top-k0; token t takes
+      the first min(k, |S|) experts of its own order that lie in S.
+  R5  budget(m): per-token softmax over all E experts, summed over the batch
+      in token order; the m experts with the largest sum (ties to the lower
+      index) form the allowed set; token t takes the first min(k, m)
+      experts of its own order inside it.
+  R6  SwiGLU expert: y = (SiLU(x G) * (x U)) D with SiLU(z) = z / (1 + e^-z),
+      no biases; G, U are [d, I] and D is [I, d] per expert.
+  R7  Empty slots (a token with fewer than k experts) carry id -1, weight 0.
+
+Parity status of each function is listed in its docstring ("pinned by ...").
+"""
+from __future__ import annotations
+
+import numpy as np
+
+POLICY_TOPK = "topk"
+POLICY_OEA = "oea"
+POLICY_BUDGET = "budget"
+POLICY_GREEDY = "greedy"
+
+
+# ---------------------------------------------------------------- precision
+
+def widen(a: np.ndarray, dtype: str) -> np.ndarray:
+    """Exact widening to float64. ``dtype`` "bf16" means ``a`` holds uint16
+    bfloat16 bit patterns; "f32" means float32 values."""
+    a = np.asarray(a)
+    if dtype == "bf16":
+        if a.dtype != np.uint16:
+            raise TypeError("bf16 inputs are uint16 bit patterns")
+        return (a.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+    if dtype == "f32":
+        if a.dtype != np.float32:
+            raise TypeError("f32 inputs are float32")
+        return a.astype(np.float64)
+    raise ValueError(dtype)
+
+
+def _finite(*arrs):
+    for a in arrs:
+        if a is not None and not np.all(np.isfinite(a)):
+            raise ValueError("inputs must be finite")
+
+
+# -------------------------------------------------------------------- router
+
+def router_logits(x, w_g, bias, dtype: str) -> np.ndarray:
+    """Router linear projection, [Router] "Analyzing Router Inference Cost",
+    step 1: h = x W_g (per token), plus a per-expert bias (the workloads'
+    skewed router bias; None means zero). float64 result [B, E].
+
+    Pinned by: exact math.fsum of sampled entries; W_g = identity reproduces x.
+    """
+    X = widen(x, dtype)
+    W = widen(w_g, dtype)
+    _finite(X, W, bias)
+    L = X @ W
+    if bias is not None:
+        L = L + np.asarray(bias, dtype=np.float32).astype(np.float64)[None, :]
+    return L
+
+
+def softmax_row(l: np.ndarray) -> np.ndarray:
+    """Softmax over one token's logits, [Router] step 2, in float64."""
+    l = np.asarray(l, dtype=np.float64)
+    z = np.exp(l - l.max())
+    return z / z.sum()
+
+
+# ----------------------------------------------------------------- ranking
+
+def token_order(l32: np.ndarray) -> np.ndarray:
+    """All experts of one token, best first (reading R1).
+
+    Primary key: logit descending; secondary: expert index ascending.
+    Negating a float32 is exact and maps -0.0/+0.0 to values that compare
+    equal, so the index decides between them.
+
+    Pinned by: brute-force comparison of every selected/unselected pair, and
+    the hand-worked routing examples.
+    """
+    l32 = np.asarray(l32, dtype=np.float32)
+    idx = np.arange(l32.shape[0])
+    # lexsort sorts by the last key first.
+    return np.lexsort((idx, -l32.astype(np.float64)))
+
+
+def _first_in(order: np.ndarray, allowed: np.ndarray, count: int) -> list:
+    out = []
+    for e in order:
+        if allowed[e]:
+            out.append(int(e))
+            if len(out) == count:
+                break
+    return out
+
+
+def _ids_matrix(sel_lists, k: int) -> np.ndarray:
+    ids = np.full((len(sel_lists), k), -1, dtype=np.int32)
+    for t, s in enumerate(sel_lists):
+        ids[t, :len(s)] = s
+    return ids
+
+
+# --------------------------------------------------------------- policies
+
+def select_topk(L32: np.ndarray, k: int) -> np.ndarray:
+    """Standard per-token top-k ([Router] step 3). ids [B, k].
+
+    Pinned by: brute force over k-subsets; equals oea(k0 = k) and budget(E).
+    """
+    return _ids_matrix([list(token_order(l)[:k]) for l in L32], k)
+
+
+def oea_active_set(L32: np.ndarray, k0: int) -> np.ndarray:
+    """[OEA]: the union over the batch of each token's k0 most important
+    experts (reading R4). Boolean mask [E].
+
+    Pinned by: brute force (smallest set holding every token's top-k0),
+    |S(k0)| <= |S_topk|, S(k0) subset of S(k0+1).
+    """
+    B, E = L32.shape
+    S = np.zeros(E, dtype=bool)
+    for l in L32:
+        S[token_order(l)[:k0]] = True
+    return S
+
+
+def select_oea(L32: np.ndarray, k: int, k0: int) -> np.ndarray:
+    """[OEA] piggyback re-route (reading R4): keep the top-k0, then fill up to
+    k slots with the token's highest-scored experts among those the batch
+    already loads. ids [B, k], -1 padded.
+
+    Pinned by: oea(k) == topk; each token keeps its own top-k0; every expert
+    of S gets a token; brute force (retained mass is maximal within S).
+    """
+    if not 1 <= k0 <= k:
+        raise ValueError("k0 must be in [1, k]")
+    S = oea_active_set(L32, k0)
+    return _ids_matrix([_first_in(token_order(l), S, k) for l in L32], k)
+
+
+def budget_mass(L32: np.ndarray) -> np.ndarray:
+    """[XShare] total gating score per expert: sum over tokens (in token
+    order) of each token's full softmax (reading R5). float64 [E].
+
+    Pinned by: sums to B; brute-force optimality of the top-m set.
+    """
+    M = np.zeros(L32.shape[1], dtype=np.float64)
+    for l in L32:
+        M += softmax_row(np.asarray(l, dtype=np.float32).astype(np.float64))
+    return M
+
+
+def budget_set(mass: np.ndarray, m: int) -> np.ndarray:
+    """The m experts of largest mass, ties to the lower index, decided on the
+    float32-rounded masses (reading R2). Boolean mask [E]."""
+    m32 = np.asarray(mass, dtype=np.float64).astype(np.float32)
+    order = np.lexsort((np.arange(m32.shape[0]), -m32.astype(np.float64)))
+    S = np.zeros(m32.shape[0], dtype=bool)
+    S[order[:m]] = True
+    return S
+
+
+def select_budget(L32: np.ndarray, k: int, m: int, mass=None) -> np.ndarray:
+    """budget(m): [XShare] modular objective with a cardinality budget
+    (reading R5). ids [B, k], -1 padded.
+
+    Pinned by: brute force over all m-subsets (total gating score is
+    maximal); budget(E) == topk; the (k/m) bound on retained top-k mass.
+    """
+    B, E = L32.shape
+    if not 1 <= m <= E:
+        raise ValueError("m must be in [1, E]")
+    if mass is None:
+        mass = budget_mass(L32)
+    S = budget_set(mass, m)
+    return _ids_matrix([_first_in(token_order(l), S, k) for l in L32], k)
+
+
+def greedy_retained_set(L32: np.ndarray, k: int, m: int) -> np.ndarray:
+    """Greedy maximisation of the retained top-k gating mass
+    F(S) = sum_t (sum of token t's k largest probabilities inside S), one
+    expert at a time, [XShare] "greedy algorithms ... maximizing the total
+    gating score". Marginal gains are compared on float32-rounded values,
+    ties to the lower index (reading R2). Boolean mask [E].
+
+    Pinned by: brute force on tiny inputs (1 - 1/e bound), and equality with
+    budget(m) when m <= k (F is then modular on |S| <= k).
+    """
+    B, E = L32.shape
+    P = np.stack([softmax_row(np.asarray(l, np.float32).astype(np.float64)) for l in L32])
+    S = np.zeros(E, dtype=bool)
+
+    def F(mask):
+        tot = 0.0
+        for t in range(B):
+            v = np.sort(P[t][mask])[::-1][:k]
+            tot += v.sum()
+        return tot
+
+    base = 0.0
+    for _ in range(m):
+        best_e, best_gain = -1, None
+        for e in range(E):
+            if S[e]:
+                continue
+            S[e] = True
+            gain = np.float32(F(S) - base)
+            S[e] = False
+            if best_gain is None or gain > best_gain:
+                best_e, best_gain = e, gain
+        S[best_e] = True
+        base = F(S)
+    return S
+
+
+def select_greedy(L32: np.ndarray, k: int, m: int) -> np.ndarray:
+    S = greedy_retained_set(L32, k, m)
+    return _ids_matrix([_first_in(token_order(l), S, k) for l in L32], k)
+
+
+def select(L32: np.ndarray, policy: str, k: int, k0: int = 0, m: int = 0):
+    """Dispatch on policy name. Returns (ids [B,k] int32, mass or None)."""
+    L32 = np.asarray(L32, dtype=np.float32)
+    _finite(L32)
+    B, E = L32.shape
+    if not 1 <= k <= E:
+        raise ValueError("k must be in [1, E]")
+    if policy == POLICY_TOPK:
+        return select_topk(L32, k), None
+    if policy == POLICY_OEA:
+        return select_oea(L32, k, k0), None
+    if policy == POLICY_BUDGET:
+        M = budget_mass(L32)
+        return select_budget(L32, k, m, M), M
+    if policy == POLICY_GREEDY:
+        return select_greedy(L32, k, m), None
+    raise ValueError(policy)
+
+
+# ------------------------------------------------------------ gate weights
+
+def gate_weights(L32: np.ndarray, ids: np.ndarray) -> np.ndarray:
+    """Renormalised gate weights (reading R3): softmax over the selected
+    logits only, float64 [B, k], 0 on empty slots.
+
+    Pinned by: sums to 1; equals p[sel] / p[sel].sum() from the full softmax.
+    """
+    B, k = ids.shape
+    W = np.zeros((B, k), dtype=np.float64)
+    for t in range(B):
+        sel = [int(e) for e in ids[t] if e >= 0]
+        if not sel:
+            continue
+        v = np.asarray(L32[t], dtype=np.float32).astype(np.float64)[sel]
+        z = np.exp(v - v[0])  # slot 0 holds the largest selected logit
+        W[t, :len(sel)] = z / z.sum()
+    return W
+
+
+# -------------------------------------------------------------- compaction
+
+def compact(ids: np.ndarray, E: int) -> dict:
+    """Active expert list and per-expert token lists ([Lynx] section 2.2: the
+    batch activates a consolidated set; only it is streamed).
+
+    active[E]     ascending expert ids with >= 1 token, then -1
+    n_active      number of such experts
+    offsets[E+1]  CSR offsets over the active list, padded with the total
+    pair_token/pair_slot [B*k]  tokens ascending within each expert, then -1
+
+    Pinned by: pairs are a permutation of the non-empty slots; the active
+    list is the sorted union.
+    """
+    B, k = ids.shape
+    used = np.zeros(E, dtype=bool)
+    for t in range(B):
+        for j in range(k):
+            if ids[t, j] >= 0:
+                used[ids[t, j]] = True
+    active = [e for e in range(E) if used[e]]
+    offsets = [0]
+    ptok, pslot = [], []
+    for e in active:
+        for t in range(B):
+            for j in range(k):
+                if ids[t, j] == e:
+                    ptok.append(t)
+                    pslot.append(j)
+        offsets.append(len(ptok))
+    n = len(active)
+    out_active = np.full(E, -1, dtype=np.int32)
+    out_active[:n] = active
+    out_off = np.full(E + 1, offsets[-1], dtype=np.int32)
+    out_off[:n + 1] = offsets
+    out_tok = np.full(B * k, -1, dtype=np.int32)
+    out_slot = np.full(B * k, -1, dtype=np.int32)
+    out_tok[:len(ptok)] = ptok
+    out_slot[:len(pslot)] = pslot
+    return {"n_active": n, "active": out_active, "offsets": out_off,
+            "pair_token": out_tok, "pair_slot": out_slot}
+
+
+# --------------------------------------------------------------------- FFN
+
+def silu(z: np.ndarray) -> np.ndarray:
+    """SiLU(z) = z / (1 + e^-z) (reading R6)."""
+    with np.errstate(over="ignore"):
+        return z / (1.0 + np.exp(-z))
+
+
+def expert_ffn(x, ids, W, w_gate, w_up, w_down, dtype: str, tokens=None) -> np.ndarray:
+    """Weighted sum of SwiGLU experts per token (reading R6), streaming only
+    the experts some token selected. float64 [B, d]; rows not in ``tokens``
+    (when given) are left zero.
+
+    Pinned by: one expert reduces to a dense SwiGLU from plain matmuls;
+    outputs are linear in D; experts no token selected do not matter.
+    """
+    X = widen(x, dtype)
+    B, d = X.shape
+    Y = np.zeros((B, d), dtype=np.float64)
+    want = np.ones(B, dtype=bool) if tokens is None else np.isin(np.arange(B), tokens)
+    needed = sorted({int(e) for t in range(B) if want[t] for e in ids[t] if e >= 0})
+    for e in needed:
+        G = widen(w_gate[e], dtype)
+        U = widen(w_up[e], dtype)
+        D = widen(w_down[e], dtype)
+        for t in range(B):
+            if not want[t]:
+                continue
+            for j in range(ids.shape[1]):
+                if ids[t, j] == e:
+                    h = silu(X[t] @ G) * (X[t] @ U)
+                    Y[t] += W[t, j] * (h @ D)
+    return Y
+
+
+# ------------------------------------------------------------------- layer
+
+def moe_layer(x, w_g, bias, w_gate, w_up, w_down, dtype: str, policy: str,
+              k: int, k0: int = 0, m: int = 0, tokens=None) -> dict:
+    """The whole decode MoE layer: router, selection, weights, compaction,
+    expert FFN. Selection runs on the float32-rounded logits (reading R2)."""
+    L = router_logits(x, w_g, bias, dtype)
+    L32 = L.astype(np.float32)
+    ids, mass = select(L32, policy, k, k0, m)
+    W = gate_weights(L32, ids)
+    c = compact(ids, L.shape[1])
+    y = expert_ffn(x, ids, W, w_gate, w_up, w_down, dtype, tokens)
+    out = {"logits": L, "logits32": L32, "ids": ids, "w": W, "mass": mass, "y": y}
+    out.update(c)
+    return out
