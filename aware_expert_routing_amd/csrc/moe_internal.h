@@ -1,0 +1,86 @@
+// Internal declarations shared by the host entry points and the kernel
+// translation units of libmoe_decode. Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/moe_decode.h"
+
+namespace moe {
+
+// ---------------------------------------------------------------- envelope
+constexpr int kMaxB = 256;
+constexpr int kMaxE = 256;
+constexpr int kMaxK = 16;
+constexpr int kMaxDim = 16384;
+
+// Router: rows of W_g per partial-sum slice.
+constexpr int kRouterRows = 32;
+
+// Expert FFN tiling (bf16 path). A work item is one active expert times one
+// strip of kStripCols output columns times one slice of the reduction.
+constexpr int kStripCols = 64;
+constexpr int kUpMaxSlices = 8;     // reduction (d) slices of the gate/up product
+constexpr int kUpSliceMin = 512;    // rows per slice before the slice count grows
+constexpr int kStageRows = 64;      // weight rows staged in LDS per pipeline stage
+
+inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
+
+// Workspace carve-up. Every segment starts on a 256-byte boundary.
+struct Workspace {
+  size_t router_part;  // float [router_slices][B][E]
+  size_t up_part;      // float [up_slices][2][B*k][I]   (gate, up partial sums)
+  size_t h;            // bf16 or float [B*k][I]
+  size_t down_part;    // float [B][k][d]
+  size_t total;
+  int router_slices;
+  int up_slices;
+  int up_slice_rows;
+};
+
+inline size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
+
+inline Workspace plan_workspace(int B, int d, int E, int I, int k, moe_dtype_t dt) {
+  Workspace w{};
+  w.router_slices = ceil_div(d, kRouterRows);
+  int slices = ceil_div(d, kUpSliceMin);
+  if (slices > kUpMaxSlices) slices = kUpMaxSlices;
+  int rows = ceil_div(d, slices);
+  rows = ceil_div(rows, kStageRows) * kStageRows;
+  w.up_slices = ceil_div(d, rows);
+  w.up_slice_rows = rows;
+  const size_t P = size_t(B) * size_t(k);
+  const size_t esz = (dt == MOE_BF16) ? 2 : 4;
+  size_t off = 0;
+  w.router_part = off;
+  off = align256(off + size_t(w.router_slices) * B * E * sizeof(float));
+  w.up_part = off;
+  off = align256(off + size_t(w.up_slices) * 2 * P * I * sizeof(float));
+  w.h = off;
+  off = align256(off + P * I * esz);
+  w.down_part = off;
+  off = align256(off + P * size_t(d) * sizeof(float));
+  w.total = off;
+  return w;
+}
+
+// ------------------------------------------------------------- launchers
+// Each launcher enqueues on `s` and returns hipGetLastError().
+
+hipError_t launch_router(const void *x, const void *w_g, moe_dtype_t dt, int B, int d, int E,
+                         float *part, int slices, hipStream_t s);
+hipError_t launch_router_reduce(const float *part, const float *bias, int slices, int B, int E,
+                                float *logits, hipStream_t s);
+
+// Selection on float32 logits[B,E].
+hipError_t launch_select(const float *logits, int B, int E, moe_policy_t p,
+                         const moe_routing_t &r, hipStream_t s);
+
+hipError_t launch_expert_ffn(const void *x, const void *w_gate, const void *w_up,
+                             const void *w_down, moe_dtype_t dt, int B, int d, int E, int I,
+                             int k, const moe_routing_t &r, void *y, char *ws,
+                             const Workspace &plan, hipStream_t s);
+
+}  // namespace moe

@@ -1,0 +1,261 @@
+#!/usr/bin/env python
+"""Benchmark of the decode MoE layer with batch-aware expert selection on one
+MI355X: layer latency, active-expert count and expert-weight HBM bandwidth.
+
+One step = one moe_layer_decode call (router, selection, gate weights,
+compaction, grouped SwiGLU FFN) over one batch of seeded synthetic tokens.
+Steps are replayed from HIP graphs and rotate over R bit-identical copies of
+the weights at different addresses, so the 256 MB Infinity Cache cannot serve
+the active experts from one step to the next. Inputs are resident in HBM
+before the timed region starts.
+
+Prints one JSON line (rank 0, N = 1). `value` is the active-expert weight
+bytes of one step divided by the measured step time (GB/s).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBPS = 8000.0
+METRIC = "MoE-layer decode µs + expert-weight HBM GB/s (% of peak), B=16, E=128 k=8"
+
+
+def _parse():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--config", default="qwen3_30b_bf16")
+    ap.add_argument("--batch", type=int, default=16)
+    ap.add_argument("--policy", default="oea", choices=["topk", "oea", "budget"])
+    ap.add_argument("--k0", type=int, default=4)
+    ap.add_argument("--m", type=int, default=32)
+    ap.add_argument("--rotate-bytes", type=float, default=2.0e9,
+                    help="replicas are added until they hold this many distinct active bytes")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--sweep", default=None,
+                    help="run every configured (config, B, policy) case; one JSON line each to this file")
+    return ap.parse_args()
+
+
+def _percentiles(v):
+    v = np.sort(np.asarray(v))
+    return float(np.median(v)), float(np.percentile(v, 10)), float(np.percentile(v, 90))
+
+
+class Case:
+    """Device state for one (config, B, policy) workload."""
+
+    def __init__(self, cfg, B, policy, k0, m, inp, dev_base, rotate_bytes):
+        import torch
+        from aware_expert_routing_amd import _lib as L
+
+        self.cfg, self.B = cfg, B
+        self.policy = L.make_policy(policy, cfg.k, k0, m)
+        self.policy_name = policy
+        self.k0, self.m = k0, m
+        tdt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+        self.x = dev_base["x"][:B].contiguous()
+        self.bias = dev_base["bias"]
+        self.ws = L.alloc_workspace(B, cfg.d, cfg.E, cfg.I, cfg.k, tdt)
+        self.logits = torch.empty((B, cfg.E), dtype=torch.float32, device="cuda")
+        self.routing = L.Routing(B, cfg.E, cfg.k)
+        self.y = torch.empty((B, cfg.d), dtype=tdt, device="cuda")
+        # One eager call to learn the active set.
+        L.moe_layer_decode(self.x, dev_base["w_g"], self.bias, dev_base["w_gate"], dev_base["w_up"],
+                           dev_base["w_down"], self.policy, self.logits, self.routing, self.y, self.ws)
+        torch.cuda.synchronize()
+        self.n_active = int(self.routing.n_active.item())
+        self.active_bytes = self.n_active * cfg.expert_bytes
+        self.pairs = int(self.routing.expert_offsets[self.n_active].item())
+        reps = max(2, math.ceil(rotate_bytes / max(1, self.active_bytes)))
+        pool = cfg.E * cfg.expert_bytes
+        reps = min(reps, max(2, int(48e9 // pool)))
+        self.replicas = [dev_base] + [{k: (v.clone() if k in ("w_g", "w_gate", "w_up", "w_down") else v)
+                                       for k, v in dev_base.items()} for _ in range(reps - 1)]
+        self.L = L
+
+    def layer(self, rep):
+        d = self.replicas[rep]
+        self.L.moe_layer_decode(self.x, d["w_g"], self.bias, d["w_gate"], d["w_up"], d["w_down"],
+                                self.policy, self.logits, self.routing, self.y, self.ws)
+
+    def ffn(self, rep):
+        d = self.replicas[rep]
+        self.L.moe_expert_ffn(self.x, d["w_gate"], d["w_up"], d["w_down"], self.routing, self.y, self.ws)
+
+
+def _capture(fn, n):
+    import torch
+    graphs = []
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for r in range(n):  # warm the code paths outside capture
+            fn(r)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    for r in range(n):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            fn(r)
+        graphs.append(g)
+    torch.cuda.synchronize()
+    return graphs
+
+
+def _time_graphs(graphs, steps, warmup):
+    """Per-step times (ms) from events recorded between graph replays on the
+    replay stream, plus the total over the timed region."""
+    import torch
+    n = len(graphs)
+    for i in range(warmup):
+        graphs[i % n].replay()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    ev[0].record()
+    for i in range(steps):
+        graphs[i % n].replay()
+        ev[i + 1].record()
+    torch.cuda.synchronize()
+    per = [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]
+    return per, ev[0].elapsed_time(ev[-1])
+
+
+def _cpu_baseline(cfg, inp, B, policy, k0, m, active_bytes, seconds):
+    from threadpoolctl import threadpool_info
+    from oracle import moe_oracle as orc
+
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    args = (inp["x"][:B], inp["w_g"], inp["bias"], inp["w_gate"], inp["w_up"], inp["w_down"],
+            cfg.dtype, policy, cfg.k, k0, m)
+    times = []
+    t_end = time.perf_counter() + seconds
+    while True:
+        t0 = time.perf_counter()
+        orc.moe_layer(*args)
+        times.append(time.perf_counter() - t0)
+        if time.perf_counter() > t_end or len(times) >= 50:
+            break
+    med = float(np.median(times))
+    return {"value": active_bytes / med / 1e9, "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{len(times)} full oracle layer calls (numpy float64: router, selection, SwiGLU "
+                      f"over the active experts with bf16 widening) on the same B={B} batch; "
+                      f"median {med * 1e3:.1f} ms per call"}
+
+
+def _run_case(cfg, B, policy, k0, m, inp, dev, args, with_cpu):
+    import torch
+
+    c = Case(cfg, B, policy, k0, m, inp, dev, args.rotate_bytes)
+    R = len(c.replicas)
+    g_layer = _capture(c.layer, R)
+    per, total = _time_graphs(g_layer, args.steps, args.warmup)
+    med, p10, p90 = _percentiles(per)
+    ms_per_step = total / args.steps
+    g_ffn = _capture(c.ffn, R)
+    per_f, total_f = _time_graphs(g_ffn, args.steps, args.warmup)
+    ffn_med, _, _ = _percentiles(per_f)
+    ffn_ms = total_f / args.steps
+    del g_layer, g_ffn
+    value = c.active_bytes / (ms_per_step * 1e-3) / 1e9
+    ffn_gbps = c.active_bytes / (ffn_ms * 1e-3) / 1e9
+    pol = policy + (f"(k0={k0})" if policy == "oea" else f"(m={m})" if policy == "budget" else "")
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic (seeded; shapes and distributions of the named layer)",
+        "config": {"workload": f"{cfg.name} decode MoE layer, B={B}, d={cfg.d}, E={cfg.E}, k={cfg.k}, "
+                               f"I={cfg.I}, policy {pol}",
+                   "batch": B, "policy": pol, "replicas": R},
+        "layer_us": {"median": round(med * 1e3, 2), "p10": round(p10 * 1e3, 2),
+                     "p90": round(p90 * 1e3, 2), "mean": round(ms_per_step * 1e3, 2)},
+        "n_active": c.n_active,
+        "pairs": c.pairs,
+        "active_expert_bytes": c.active_bytes,
+        "pct_of_hbm_peak": round(100 * value / PEAK_HBM_GBPS, 2),
+        "expert_ffn_us": round(ffn_ms * 1e3, 2),
+        "roofline": {"bound": "hbm", "achieved": round(ffn_gbps, 1), "peak": PEAK_HBM_GBPS,
+                     "unit": "GB/s", "frac": round(ffn_gbps / PEAK_HBM_GBPS, 4), "traffic": None,
+                     "kernel": "expert FFN (moe_expert_ffn: gate/up, SwiGLU, down, combine)",
+                     "bytes_per_launch": c.active_bytes},
+    }
+    if with_cpu:
+        out["cpu_baseline"] = _cpu_baseline(cfg, inp, B, policy, k0, m, c.active_bytes, args.cpu_seconds)
+    del c
+    torch.cuda.empty_cache()
+    return out
+
+
+def _upload(inp, dtype):
+    import torch
+
+    def up(a):
+        if a is None:
+            return None
+        if dtype == "bf16" and a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+        return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    return {k: up(v) for k, v in inp.items()}
+
+
+def main():
+    args = _parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: this build has no multi-GPU path "
+              f"(asked for --gpus {args.gpus}).", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from aware_expert_routing_amd.workloads import CONFIGS, make_layer
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    if args.sweep:
+        with open(args.sweep, "w") as f:
+            for cname, cfg in CONFIGS.items():
+                inp = make_layer(cfg, max(cfg.batches))
+                dev = _upload(inp, cfg.dtype)
+                pols = [("topk", 0, 0)] + [("oea", k0, 0) for k0 in cfg.oea_k0] + \
+                       [("budget", 0, m) for m in cfg.budget_m]
+                for B in cfg.batches:
+                    for pol, k0, m in pols:
+                        rec = _run_case(cfg, B, pol, k0, m, inp, dev, args, with_cpu=False)
+                        f.write(json.dumps(rec) + "\n")
+                        f.flush()
+                        print(f"{cname} B={B} {pol}{k0 or m or ''}: n_active={rec['n_active']} "
+                              f"layer {rec['layer_us']['median']} us, {rec['value']} GB/s, "
+                              f"ffn {rec['roofline']['achieved']} GB/s", flush=True)
+                del dev
+                torch.cuda.empty_cache()
+        return
+    cfg = CONFIGS[args.config]
+    inp = make_layer(cfg, max(args.batch, max(cfg.batches)))
+    dev = _upload(inp, cfg.dtype)
+    rec = _run_case(cfg, args.batch, args.policy, args.k0, args.m, inp, dev, args,
+                    with_cpu=not args.no_cpu_baseline)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

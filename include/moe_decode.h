@@ -1,0 +1,145 @@
+/*
+ * moe_decode.h -- C ABI of the decode-time MoE layer with batch-aware expert
+ * selection, for AMD Instinct MI355X (gfx950).
+ *
+ * The layer (one decode step, B tokens):
+ *   1. router:    logits[t,e] = sum_i x[t,i] * W_g[i,e] + bias[e]
+ *                 ("Router Caching and Optimization", section "Analyzing
+ *                 Router Inference Cost", step 1, linear projection).
+ *   2. ranking:   each token orders the experts by logit, highest first, ties
+ *                 to the lower index; softmax and top-k follow from it (same
+ *                 section, steps 2 and 3).
+ *   3. re-route:  a batch-level policy shrinks the set of experts the batch
+ *                 activates:
+ *                   TOPK       standard per-token top-k;
+ *                   OEA(k0)    each token keeps its top-k0; S is the union of
+ *                              these over the batch; each token then takes its
+ *                              highest-ranked experts inside S, up to k
+ *                              ("Opportunistic Expert Activation", abstract);
+ *                   BUDGET(m)  the m experts with the largest softmax mass
+ *                              summed over the batch form the allowed set; each
+ *                              token takes its top min(k,m) inside it ("XShare",
+ *                              abstract: maximise the total gating score).
+ *   4. weights:   gate weights are the softmax over each token's selected
+ *                 logits (renormalised); empty slots weigh 0.
+ *   5. compaction: the ascending list of active experts and, per active
+ *                 expert, its tokens in ascending order ("Lynx", Technical
+ *                 Summary 2.2: the batch activates one consolidated set).
+ *   6. expert FFN: y[t] = sum_j w[t,j] * (SiLU(x_t G_e) * (x_t U_e)) D_e with
+ *                 e the expert in slot j, SiLU(z) = z / (1 + exp(-z)); only the
+ *                 active experts' weights are read from HBM ("Lynx", Technical
+ *                 Summary 1: latency follows the number of distinct experts).
+ *
+ * Conventions for every entry point:
+ *   - Array pointers are DEVICE pointers to contiguous row-major arrays,
+ *     owned by the caller. The library keeps no pointer after it returns.
+ *   - x, w_g, w_gate, w_up, w_down and y share one element type, `dt`
+ *     (MOE_F32: float; MOE_BF16: bfloat16 bit patterns, uint16). Logits,
+ *     bias, gate weights and batch masses are always float32; ids int32.
+ *   - Layouts: x[B,d], w_g[d,E], bias[E], w_gate[E,d,I], w_up[E,d,I],
+ *     w_down[E,I,d], logits[B,E], y[B,d].
+ *   - `stream` is a hipStream_t (NULL: the default stream). Calls only
+ *     enqueue work and return; results are valid once the stream reaches
+ *     them. No call allocates, frees or synchronises, so calls can be
+ *     captured into a HIP graph.
+ *   - Every argument is checked on the host before any HIP call; a failed
+ *     check returns an error code and enqueues nothing. No C++ exception
+ *     crosses this interface. Calls hold no global state and are safe from
+ *     several host threads on different streams with different workspaces.
+ *   - Non-finite inputs give unspecified results.
+ *
+ * Supported envelope (else MOE_ERR_UNSUPPORTED): 1 <= B <= 256,
+ * 1 <= E <= 256, 1 <= k <= 16, 8 <= d <= 16384 and 8 <= I <= 16384 with d and
+ * I multiples of 8. Pointers to x, w_g, w_gate, w_up, w_down and y must be
+ * 16-byte aligned (else MOE_ERR_INVALID_ARG).
+ */
+#ifndef MOE_DECODE_H
+#define MOE_DECODE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = 1, /* null/misaligned pointer, k > E, k0 or m out of range, ... */
+  MOE_ERR_UNSUPPORTED = 2, /* sizes outside the supported envelope above              */
+  MOE_ERR_WORKSPACE = 3,   /* workspace missing, misaligned or smaller than required  */
+  MOE_ERR_HIP = 4          /* a kernel launch failed (hipGetLastError)                 */
+} moe_status_t;
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype_t;
+
+typedef enum {
+  MOE_POLICY_TOPK = 0,   /* k experts per token (k <= E)                         */
+  MOE_POLICY_OEA = 1,    /* 1 <= k0 <= k; tokens get min(k, |S|) experts         */
+  MOE_POLICY_BUDGET = 2  /* 1 <= m <= E; tokens get min(k, m) experts            */
+} moe_policy_kind_t;
+
+/* Selection policy. k0 is read only by OEA, m only by BUDGET. */
+typedef struct {
+  int32_t kind; /* moe_policy_kind_t */
+  int32_t k;
+  int32_t k0;
+  int32_t m;
+} moe_policy_t;
+
+/* Routing outputs (device pointers, caller-owned, written in full by every
+ * call that produces them; sizes use the call's B, E and k). */
+typedef struct {
+  int32_t *topk_ids;       /* [B,k] slot order = logit desc, index asc; -1 = empty */
+  float *topk_w;           /* [B,k] renormalised gate weight; 0 for empty slots    */
+  int32_t *n_active;       /* [1]   experts that receive >= 1 token                */
+  int32_t *active_experts; /* [E]   ascending expert ids, then -1                  */
+  int32_t *expert_offsets; /* [E+1] CSR offsets over the active list; entries past
+                                    n_active repeat the number of pairs           */
+  int32_t *pair_token;     /* [B*k] token of each (expert, token) pair, tokens
+                                    ascending within an expert; then -1           */
+  int32_t *pair_slot;      /* [B*k] slot j of that pair in topk_ids; then -1        */
+  float *batch_mass;       /* [E]   BUDGET: sum over tokens of softmax(logits_t);
+                                    may be NULL (other policies leave it alone)   */
+} moe_routing_t;
+
+/* Bytes of workspace the calls below need for these sizes (256-byte aligned
+ * base required). Returns 0 when the sizes are outside the envelope. The same
+ * workspace may serve consecutive calls on one stream; calls that may overlap
+ * need separate workspaces. Contents need no initialisation. */
+size_t moe_workspace_bytes(int B, int d, int E, int I, int k, moe_dtype_t dt);
+
+/* Step 1 only: logits[B,E] (float32) = x W_g + bias. bias may be NULL (zero).
+ * Uses the workspace for per-slice partial sums. */
+moe_status_t moe_route(const void *x, const void *w_g, const float *bias, moe_dtype_t dt,
+                       int B, int d, int E, float *logits, void *workspace,
+                       size_t workspace_bytes, void *stream);
+
+/* Steps 2-5 on given float32 logits[B,E]: writes every field of *out.
+ * BUDGET requires out->batch_mass. Needs no workspace. */
+moe_status_t moe_select(const float *logits, int B, int E, moe_policy_t policy,
+                        const moe_routing_t *out, void *stream);
+
+/* Step 6 for routing produced by moe_select (same B, E, k): y[B,d] in dt.
+ * Reads only the weights of the first *n_active experts of the active list. */
+moe_status_t moe_expert_ffn(const void *x, const void *w_gate, const void *w_up,
+                            const void *w_down, moe_dtype_t dt, int B, int d, int E, int I,
+                            int k, const moe_routing_t *routing, void *y, void *workspace,
+                            size_t workspace_bytes, void *stream);
+
+/* Steps 1-6: the whole decode MoE layer. logits[B,E] receives the router
+ * output; *routing receives the selection as moe_select writes it. */
+moe_status_t moe_layer_decode(const void *x, const void *w_g, const float *bias,
+                              const void *w_gate, const void *w_up, const void *w_down,
+                              moe_dtype_t dt, int B, int d, int E, int I, moe_policy_t policy,
+                              float *logits, const moe_routing_t *routing, void *y,
+                              void *workspace, size_t workspace_bytes, void *stream);
+
+/* Static description of a status code. Never NULL. */
+const char *moe_status_string(moe_status_t status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_DECODE_H */

@@ -1,0 +1,119 @@
+"""Helpers of the GPU parity tests: device upload of seeded inputs, calls
+through the C ABI (via the ctypes binding) and comparisons with the oracle.
+
+Tolerances (bf16 weights, float32 accumulation): logits per row within
+1e-5 * max(1, max|L_ref|); gate weights within 1e-6 relative; layer output
+max |dy| <= 2e-2 and ||dy||_2 / ||y_ref||_2 <= 1e-2. float32 layers: output
+max |dy| <= 1e-5 * max|y_ref| and relative L2 <= 1e-5. Routing (ids, active
+list, offsets, pairs) must be bit-exact.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from aware_expert_routing_amd import _lib as L
+
+LOGIT_RTOL = 1e-5
+W_RTOL = 1e-6
+BF16_MAX_ABS = 2e-2
+BF16_REL_L2 = 1e-2
+F32_REL = 1e-5
+
+GUARD = 64  # sentinel elements after every output buffer
+
+
+def to_dev(a, dtype: str):
+    if a is None:
+        return None
+    if dtype == "bf16" and a.dtype == np.uint16:
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def bf16_bits(t: torch.Tensor) -> np.ndarray:
+    return t.detach().contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def y_to_f64(y: torch.Tensor) -> np.ndarray:
+    return y.detach().float().cpu().numpy().astype(np.float64)
+
+
+class Guarded:
+    """A device buffer followed by sentinel elements that no call may touch."""
+
+    def __init__(self, shape, dtype, fill):
+        n = int(np.prod(shape))
+        self.full = torch.full((n + GUARD,), fill, dtype=dtype, device="cuda")
+        self.fill = fill
+        self.t = self.full[:n].view(shape)
+
+    def intact(self) -> bool:
+        tail = self.full[-GUARD:].float().cpu()
+        return bool(torch.all(tail == float(self.fill)))
+
+
+def policy_args(policy: str, p: int):
+    if policy == "topk":
+        return dict(policy="topk", k0=0, m=0)
+    if policy == "oea":
+        return dict(policy="oea", k0=p, m=0)
+    if policy == "budget":
+        return dict(policy="budget", k0=0, m=p)
+    raise ValueError(policy)
+
+
+def routing_numpy(r: L.Routing) -> dict:
+    out = {
+        "ids": r.topk_ids.cpu().numpy(),
+        "w": r.topk_w.cpu().numpy().astype(np.float64),
+        "n_active": int(r.n_active.cpu().item()),
+        "active": r.active_experts.cpu().numpy(),
+        "offsets": r.expert_offsets.cpu().numpy(),
+        "pair_token": r.pair_token.cpu().numpy(),
+        "pair_slot": r.pair_slot.cpu().numpy(),
+    }
+    if r.batch_mass is not None:
+        out["mass"] = r.batch_mass.cpu().numpy().astype(np.float64)
+    return out
+
+
+def weight_rtol_from_logits(Lg: np.ndarray, Lref: np.ndarray) -> np.ndarray:
+    """Per-token relative tolerance of the gate weights when the two sides
+    rank different float32 logits. With every selected logit off by at most
+    eps, w_j' = w_j e^{d_j} / sum_i w_i e^{d_i} lies within w_j e^{+-2 eps},
+    so |dw_j| <= (e^{2 eps} - 1) w_j; W_RTOL covers float32 rounding."""
+    eps = np.abs(Lg.astype(np.float64) - Lref).max(axis=1)
+    return (np.expm1(2 * eps) + W_RTOL)[:, None]
+
+
+def assert_routing_equal(g: dict, o: dict, tag: str = "", w_rtol=None):
+    assert g["n_active"] == o["n_active"], f"{tag} n_active gpu={g['n_active']} oracle={o['n_active']}"
+    np.testing.assert_array_equal(g["ids"], o["ids"], err_msg=f"{tag} topk_ids")
+    np.testing.assert_array_equal(g["active"], o["active"], err_msg=f"{tag} active_experts")
+    np.testing.assert_array_equal(g["offsets"], o["offsets"], err_msg=f"{tag} expert_offsets")
+    np.testing.assert_array_equal(g["pair_token"], o["pair_token"], err_msg=f"{tag} pair_token")
+    np.testing.assert_array_equal(g["pair_slot"], o["pair_slot"], err_msg=f"{tag} pair_slot")
+    if w_rtol is None:
+        np.testing.assert_allclose(g["w"], o["w"], rtol=W_RTOL, atol=1e-7, err_msg=f"{tag} topk_w")
+    else:
+        bad = np.abs(g["w"] - o["w"]) > w_rtol * np.abs(o["w"]) + 1e-7
+        assert not bad.any(), f"{tag} topk_w: {int(bad.sum())} weights beyond the logit-derived bound"
+
+
+def assert_logits_close(Lg: np.ndarray, Lref: np.ndarray, tag: str = ""):
+    scale = np.maximum(1.0, np.abs(Lref).max(axis=1))
+    err = np.abs(Lg.astype(np.float64) - Lref).max(axis=1)
+    worst = float((err / scale).max())
+    assert worst <= LOGIT_RTOL, f"{tag} logits rel err {worst:.3e}"
+
+
+def assert_y_close(yg: np.ndarray, yref: np.ndarray, dtype: str, tag: str = ""):
+    d = yg - yref
+    rel = float(np.linalg.norm(d) / max(np.linalg.norm(yref), 1e-30))
+    mx = float(np.abs(d).max())
+    if dtype == "bf16":
+        assert mx <= BF16_MAX_ABS and rel <= BF16_REL_L2, f"{tag} max|dy|={mx:.3e} relL2={rel:.3e}"
+    else:
+        assert mx <= F32_REL * float(np.abs(yref).max()) and rel <= F32_REL, \
+            f"{tag} max|dy|={mx:.3e} relL2={rel:.3e}"

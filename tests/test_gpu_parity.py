@@ -1,0 +1,266 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Cases cover the five workload shapes at their configured batches and
+policies, standalone selection on seeded logits (including exact ties and
+signed zeros), ragged sizes, experts with more than 64 tokens, the maximum
+envelope and degenerate layers. Expected values always come from the
+oracle run on the same seeded inputs; tolerances are in gpu_helpers.
+"""
+import functools
+
+import numpy as np
+import pytest
+import torch
+
+from aware_expert_routing_amd import _lib as L
+from aware_expert_routing_amd.workloads import (CONFIGS, LayerConfig, bf16_bits_from_f32,
+                                                make_hidden, make_layer, make_logits)
+from gpu_helpers import (Guarded, assert_logits_close, assert_routing_equal, assert_y_close,
+                         policy_args, routing_numpy, to_dev, weight_rtol_from_logits, y_to_f64)
+from oracle import moe_oracle as orc
+
+pytestmark = pytest.mark.gpu
+
+
+# --------------------------------------------------------------- fixtures
+
+@functools.lru_cache(maxsize=1)
+def _layer_inputs(cname: str):
+    """Full-size seeded weights for one config, on host and device (one config
+    cached at a time to bound host memory)."""
+    cfg = CONFIGS[cname]
+    Bmax = max(cfg.batches)
+    inp = make_layer(cfg, Bmax)
+    dev = {k: to_dev(v, cfg.dtype) for k, v in inp.items()}
+    return inp, dev
+
+
+def _dtype(cfg):
+    return torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+
+
+def _run_layer(cfg: LayerConfig, inp, dev, B: int, policy: str, k0: int, m: int, guard=True):
+    tdt = _dtype(cfg)
+    x = dev["x"][:B].contiguous()
+    pol = L.make_policy(policy, cfg.k, k0, m)
+    r = L.Routing(B, cfg.E, cfg.k)
+    ws = L.alloc_workspace(B, cfg.d, cfg.E, cfg.I, cfg.k, tdt)
+    lg = Guarded((B, cfg.E), torch.float32, -7.0)
+    y = Guarded((B, cfg.d), tdt, 3.0)
+    L.moe_layer_decode(x, dev["w_g"], dev["bias"], dev["w_gate"], dev["w_up"], dev["w_down"], pol,
+                       lg.t, r, y.t, ws)
+    torch.cuda.synchronize()
+    if guard:
+        assert lg.intact() and y.intact(), "write past the end of an output buffer"
+    return lg.t.cpu().numpy(), routing_numpy(r), y.t
+
+
+def _oracle(cfg, inp, B, policy, k0, m, tokens=None):
+    return orc.moe_layer(inp["x"][:B], inp["w_g"], inp["bias"], inp["w_gate"], inp["w_up"],
+                         inp["w_down"], cfg.dtype, policy, cfg.k, k0, m, tokens=tokens)
+
+
+def _layer_cases():
+    cases = []
+    for cname, cfg in CONFIGS.items():
+        pols = [("topk", 0)] + [("oea", k0) for k0 in cfg.oea_k0] + [("budget", m) for m in cfg.budget_m]
+        for B in cfg.batches:
+            for pol, p in pols:
+                if cname == "qwen3_30b_bf16" and pol == "oea" and B != 16 and p not in (1, 4):
+                    continue  # full k0 sweep at B=16 only
+                cases.append(pytest.param(cname, B, pol, p, id=f"{cname}-B{B}-{pol}{p or ''}"))
+    return cases
+
+
+# ------------------------------------------------------------ whole layer
+
+@pytest.mark.parametrize("cname,B,policy,p", _layer_cases())
+def test_layer_matches_oracle(cname, B, policy, p):
+    cfg = CONFIGS[cname]
+    inp, dev = _layer_inputs(cname)
+    a = policy_args(policy, p)
+    print(f"\n[case] {cname} B={B} {policy}{p}", flush=True)
+    Lg, rg, y = _run_layer(cfg, inp, dev, B, a["policy"], a["k0"], a["m"])
+    # Large layers: the oracle computes a sample of tokens one by one.
+    tokens = None
+    if cfg.d * cfg.I * B > 2048 * 768 * 64:
+        tokens = sorted({0, 1, B // 2, B - 1})
+    o = _oracle(cfg, inp, B, a["policy"], a["k0"], a["m"], tokens)
+    assert_logits_close(Lg, o["logits"], cname)
+    assert_routing_equal(rg, o, cname, weight_rtol_from_logits(Lg, o["logits"]))
+    yg = y_to_f64(y)
+    rows = slice(None) if tokens is None else tokens
+    assert_y_close(yg[rows], o["y"][rows], cfg.dtype, f"{cname} B={B} {policy}{p}")
+
+
+def test_layer_is_deterministic():
+    cfg = CONFIGS["qwen3_30b_bf16"]
+    inp, dev = _layer_inputs("qwen3_30b_bf16")
+    outs = [_run_layer(cfg, inp, dev, 16, "oea", 2, 0) for _ in range(3)]
+    for Lg, rg, y in outs[1:]:
+        assert np.array_equal(Lg, outs[0][0])
+        assert np.array_equal(rg["ids"], outs[0][1]["ids"])
+        assert np.array_equal(rg["w"], outs[0][1]["w"])
+        assert torch.equal(y, outs[0][2])
+
+
+def test_route_select_ffn_equal_layer():
+    """The three standalone entry points reproduce the fused layer bit for bit."""
+    cfg = CONFIGS["lynx_bf16"]
+    inp, dev = _layer_inputs("lynx_bf16")
+    B = 16
+    Lg, rg, y = _run_layer(cfg, inp, dev, B, "budget", 0, 24)
+    x = dev["x"][:B].contiguous()
+    ws = L.alloc_workspace(B, cfg.d, cfg.E, cfg.I, cfg.k, torch.bfloat16)
+    lg = torch.empty((B, cfg.E), dtype=torch.float32, device="cuda")
+    L.moe_route(x, dev["w_g"], dev["bias"], lg, ws)
+    r = L.Routing(B, cfg.E, cfg.k)
+    L.moe_select(lg, L.make_policy("budget", cfg.k, 0, 24), r)
+    y2 = torch.empty((B, cfg.d), dtype=torch.bfloat16, device="cuda")
+    L.moe_expert_ffn(x, dev["w_gate"], dev["w_up"], dev["w_down"], r, y2, ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(lg.cpu().numpy(), Lg)
+    r2 = routing_numpy(r)
+    for key in ("ids", "w", "active", "offsets", "pair_token", "pair_slot", "mass"):
+        assert np.array_equal(r2[key], rg[key]), key
+    assert torch.equal(y2, y)
+
+
+# ------------------------------------------------------------- selection
+
+_SEL_SHAPES = [(1, 128, 8), (4, 16, 4), (3, 8, 8), (16, 64, 8), (16, 128, 8), (64, 128, 8),
+               (37, 100, 6), (256, 256, 16), (128, 64, 1)]
+
+
+def _sel_policies(E, k):
+    out = [("topk", 0)]
+    out += [("oea", k0) for k0 in sorted({1, max(1, k // 2), k})]
+    out += [("budget", m) for m in sorted({1, max(1, k - 1), max(1, E // 4), E})]
+    return out
+
+
+def _sel_cases():
+    cases = []
+    for (B, E, k) in _SEL_SHAPES:
+        for kind in ("normal", "ties", "flat"):
+            for pol, p in _sel_policies(E, k):
+                cases.append(pytest.param(B, E, k, kind, pol, p, id=f"B{B}-E{E}-k{k}-{kind}-{pol}{p or ''}"))
+    return cases
+
+
+@pytest.mark.parametrize("B,E,k,kind,policy,p", _sel_cases())
+def test_select_matches_oracle(B, E, k, kind, policy, p):
+    """Both sides rank the same float32 logits, so routing is bit-exact."""
+    Lh = make_logits(B, E, seed=11, kind=kind)
+    a = policy_args(policy, p)
+    r = L.Routing(B, E, k)
+    lg = to_dev(Lh, "f32")
+    L.moe_select(lg, L.make_policy(a["policy"], k, a["k0"], a["m"]), r)
+    torch.cuda.synchronize()
+    g = routing_numpy(r)
+    ids, M = orc.select(Lh, a["policy"], k, a["k0"], a["m"])
+    o = {"ids": ids, "w": orc.gate_weights(Lh, ids)}
+    o.update(orc.compact(ids, E))
+    if M is not None:
+        np.testing.assert_allclose(g["mass"], M, rtol=2e-6, atol=1e-12, err_msg="batch_mass")
+    assert_routing_equal(g, o, f"B{B} E{E} k{k} {kind} {policy}{p}")
+
+
+# ------------------------------------------------------------- edge cases
+
+def _custom_layer(B, d, E, I, k, dtype="bf16", seed=0, bias=None, wg_scale=1.0):
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((B, d)).astype(np.float32)
+    wg = (wg_scale * rng.standard_normal((d, E)) / np.sqrt(d)).astype(np.float32)
+    # Scaled so that x G, x U and y are O(1) at any d and I, as in the
+    # configured workloads (the absolute output tolerance assumes that).
+    G = (rng.standard_normal((E, d, I)) / np.sqrt(d)).astype(np.float32)
+    U = (rng.standard_normal((E, d, I)) / np.sqrt(d)).astype(np.float32)
+    D = (rng.standard_normal((E, I, d)) / np.sqrt(I)).astype(np.float32)
+    b = None if bias is None else np.asarray(bias, dtype=np.float32)
+    if dtype == "bf16":
+        x, wg, G, U, D = (bf16_bits_from_f32(a) for a in (x, wg, G, U, D))
+    inp = {"x": x, "w_g": wg, "bias": b, "w_gate": G, "w_up": U, "w_down": D}
+    cfg = LayerConfig(name="custom", d=d, E=E, k=k, I=I, dtype=dtype, zipf_s=0.0, batches=(B,),
+                      hidden="iid")
+    return cfg, inp, {kk: to_dev(v, dtype) for kk, v in inp.items()}
+
+
+@pytest.mark.parametrize("B,d,E,I,k,policy,p,dtype", [
+    (5, 200, 10, 72, 3, "topk", 0, "bf16"),      # ragged d and I (not multiples of 64)
+    (5, 200, 10, 72, 3, "oea", 1, "bf16"),
+    (7, 136, 12, 40, 4, "budget", 3, "bf16"),
+    (7, 136, 12, 40, 4, "oea", 2, "f32"),
+    (1, 64, 1, 64, 1, "topk", 0, "bf16"),        # one expert: a dense SwiGLU
+    (3, 64, 4, 64, 4, "topk", 0, "bf16"),        # k = E
+    (256, 64, 256, 64, 16, "topk", 0, "bf16"),   # largest B, E and k
+    (256, 64, 256, 64, 16, "oea", 3, "bf16"),
+    (256, 64, 256, 64, 16, "budget", 40, "bf16"),
+    (9, 4096, 8, 64, 2, "topk", 0, "bf16"),      # deep reduction, several d slices
+])
+def test_edge_layers(B, d, E, I, k, policy, p, dtype):
+    cfg, inp, dev = _custom_layer(B, d, E, I, k, dtype)
+    a = policy_args(policy, p)
+    Lg, rg, y = _run_layer(cfg, inp, dev, B, a["policy"], a["k0"], a["m"])
+    o = _oracle(cfg, inp, B, a["policy"], a["k0"], a["m"])
+    assert_logits_close(Lg, o["logits"])
+    assert_routing_equal(rg, o, w_rtol=weight_rtol_from_logits(Lg, o["logits"]))
+    assert_y_close(y_to_f64(y), o["y"], dtype)
+
+
+def test_expert_with_more_than_64_tokens():
+    """A dominant expert receives all 150 tokens: several 64-token passes."""
+    E = 16
+    bias = np.zeros(E, np.float32)
+    bias[5] = 30.0
+    cfg, inp, dev = _custom_layer(150, 256, E, 128, 2, "bf16", bias=bias)
+    for policy, p in (("topk", 0), ("oea", 1), ("budget", 2)):
+        a = policy_args(policy, p)
+        Lg, rg, y = _run_layer(cfg, inp, dev, 150, a["policy"], a["k0"], a["m"])
+        o = _oracle(cfg, inp, 150, a["policy"], a["k0"], a["m"])
+        assert_routing_equal(rg, o, w_rtol=weight_rtol_from_logits(Lg, o["logits"]))
+        counts = np.diff(rg["offsets"][:rg["n_active"] + 1])
+        assert counts.max() == 150
+        assert_y_close(y_to_f64(y), o["y"], "bf16")
+
+
+@pytest.mark.parametrize("T", [1, 2, 3, 4, 5, 8, 15, 16, 17, 33, 64])
+def test_token_counts_around_path_switch(T):
+    """Experts with T tokens for T around the dot/MFMA switch and tile edges."""
+    E = 4
+    bias = np.array([40.0, 0.0, 0.0, 0.0], np.float32)  # every token takes expert 0 first
+    cfg, inp, dev = _custom_layer(T, 512, E, 192, 1, "bf16", bias=bias, seed=T)
+    Lg, rg, y = _run_layer(cfg, inp, dev, T, "topk", 0, 0)
+    o = _oracle(cfg, inp, T, "topk", 0, 0)
+    assert rg["n_active"] == 1
+    assert_routing_equal(rg, o, w_rtol=weight_rtol_from_logits(Lg, o["logits"]))
+    assert_y_close(y_to_f64(y), o["y"], "bf16")
+
+
+def test_flat_router_ties():
+    """W_g = 0 and no bias: every logit is 0, ties go to the lowest indices."""
+    cfg, inp, dev = _custom_layer(8, 128, 16, 64, 4, "bf16", wg_scale=0.0)
+    for policy, p in (("topk", 0), ("oea", 1), ("budget", 6)):
+        a = policy_args(policy, p)
+        Lg, rg, y = _run_layer(cfg, inp, dev, 8, a["policy"], a["k0"], a["m"])
+        o = _oracle(cfg, inp, 8, a["policy"], a["k0"], a["m"])
+        assert np.all(Lg == 0)
+        assert_routing_equal(rg, o, w_rtol=weight_rtol_from_logits(Lg, o["logits"]))
+        assert_y_close(y_to_f64(y), o["y"], "bf16")
+
+
+def test_unselected_experts_are_not_read():
+    """Overwriting the weights of inactive experts with NaN leaves y unchanged."""
+    cfg = CONFIGS["qwen3_30b_bf16"]
+    inp, dev = _layer_inputs("qwen3_30b_bf16")
+    Lg, rg, y = _run_layer(cfg, inp, dev, 16, "oea", 2, 0)
+    act = set(rg["active"][:rg["n_active"]].tolist())
+    inactive = [e for e in range(cfg.E) if e not in act]
+    g2, u2, d2 = (dev[k].clone() for k in ("w_gate", "w_up", "w_down"))
+    for t in (g2, u2, d2):
+        t[inactive] = float("nan")
+    dev2 = dict(dev, w_gate=g2, w_up=u2, w_down=d2)
+    _, rg2, y2 = _run_layer(cfg, inp, dev2, 16, "oea", 2, 0)
+    assert torch.equal(y2, y)
+    del g2, u2, d2, dev2
+    torch.cuda.empty_cache()
