@@ -24,7 +24,7 @@ constexpr int kRouterRows = 32;
 constexpr int kStripCols = 64;
 constexpr int kUpMaxSlices = 8;     // reduction (d) slices of the gate/up product
 constexpr int kUpSliceMin = 512;    // rows per slice before the slice count grows
-constexpr int kStageRows = 64;      // weight rows staged in LDS per pipeline stage
+constexpr int kStageRows = 128;     // weight rows staged in LDS per pipeline stage
 
 inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
@@ -33,7 +33,8 @@ struct Workspace {
   size_t router_part;  // float [router_slices][B][E]
   size_t up_part;      // float [up_slices][2][B*k][I]   (gate, up partial sums)
   size_t h;            // bf16 or float [B*k][I]
-  size_t down_part;    // float [B][k][d]
+  size_t down_part;    // float [B*k][d], one row per (expert, token) pair
+  size_t pair_of_slot; // int32 [B*k]: pair index of token slot t*k+j
   size_t total;
   int router_slices;
   int up_slices;
@@ -62,6 +63,8 @@ inline Workspace plan_workspace(int B, int d, int E, int I, int k, moe_dtype_t d
   off = align256(off + P * I * esz);
   w.down_part = off;
   off = align256(off + P * size_t(d) * sizeof(float));
+  w.pair_of_slot = off;
+  off = align256(off + P * sizeof(int32_t));
   w.total = off;
   return w;
 }
