@@ -16,11 +16,16 @@
 //             the tokens of each active expert (ascending).
 //
 // Work split: the batch step couples all tokens, so one workgroup of 16 waves
-// does everything. Wave w owns tokens w, w+16, ...; each lane owns experts
-// lane, lane+64, ... A token's experts are ranked by repeated wave-wide
-// maximum of 64-bit keys (orderable logit bits << 32 | ~expert): the largest
-// key is the largest logit, and among equal logits the lowest index. Key 0
-// never occurs for a finite logit, so it marks "no candidate".
+// does everything. Wave w owns tokens w, w+16, ...; lane l owns experts l,
+// l+64, ... (NV = ceil(E/64) of them). A token's experts are ranked by
+// repeated wave-wide maxima of order-preserving 32-bit keys; among equal keys
+// the lowest expert index is read off the ballots of "key == max" (scalar
+// work). Key 0 is no finite logit's key and marks "not a candidate".
+//
+// Results stay in LDS until the last phase: per (token, slot) the expert and
+// weight, per expert a bitmask of its tokens. The position of token t in
+// expert e's list is then the number of lower tokens in that bitmask, so the
+// pair lists are written by all threads at once.
 #include "moe_internal.h"
 
 namespace moe {
@@ -28,9 +33,9 @@ namespace {
 
 constexpr int kThreads = 1024;
 constexpr int kWaves = kThreads / 64;
-constexpr int kNV = kMaxE / 64;             // experts per lane
-constexpr int kTokPerWave = kMaxB / kWaves;  // tokens per wave
+constexpr int kTokPerWave = kMaxB / kWaves;  // token slots per wave
 constexpr int kWords = kMaxE / 32;           // words of an expert bitmask
+constexpr int kTokWords = kMaxB / 32;        // words of a token bitmask
 
 // Total order on float32 as unsigned integers; -0.0 maps like +0.0.
 __device__ __forceinline__ uint32_t ord_bits(float v) {
@@ -43,55 +48,98 @@ __device__ __forceinline__ float from_ord_bits(uint32_t o) {
   return __uint_as_float((o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o);
 }
 
-__device__ __forceinline__ uint64_t make_key(float v, int e) {
-  return (uint64_t(ord_bits(v)) << 32) | uint64_t(0xFFFFFFFFu - uint32_t(e));
+// Wave-wide reductions with DPP lane moves (gfx9 encodings): quad_perm
+// [1,0,3,2] and [2,3,0,1], row_half_mirror, row_mirror, then row_bcast:15
+// into rows 1 and 3 and row_bcast:31 into rows 2 and 3. After the six steps
+// lane 63 holds the result over all 64 lanes; readlane makes it uniform.
+constexpr int kDppQuadX1 = 0xB1;
+constexpr int kDppQuadX2 = 0x4E;
+constexpr int kDppHalfMirror = 0x141;
+constexpr int kDppMirror = 0x140;
+constexpr int kDppBcast15 = 0x142;
+constexpr int kDppBcast31 = 0x143;
+
+// Lanes that a step does not write keep `old`.
+template <int CTRL, int ROWS>
+__device__ __forceinline__ uint32_t dpp(uint32_t old, uint32_t v) {
+  return uint32_t(__builtin_amdgcn_update_dpp(int(old), int(v), CTRL, ROWS, 0xF, false));
 }
 
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) {
-    const uint32_t lo = __shfl_xor(uint32_t(v), off);
-    const uint32_t hi = __shfl_xor(uint32_t(v >> 32), off);
-    const uint64_t o = (uint64_t(hi) << 32) | lo;
-    v = o > v ? o : v;
-  }
-  return v;
+template <int CTRL, int ROWS>
+__device__ __forceinline__ uint32_t umax_step(uint32_t v) {
+  const uint32_t w = dpp<CTRL, ROWS>(v, v);
+  return w > v ? w : v;
 }
 
-// Butterfly sums: partner lanes add the same two values (commutative), so
-// every lane ends with the identical, run-to-run reproducible result.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = umax_step<kDppQuadX1, 0xF>(v);
+  v = umax_step<kDppQuadX2, 0xF>(v);
+  v = umax_step<kDppHalfMirror, 0xF>(v);
+  v = umax_step<kDppMirror, 0xF>(v);
+  v = umax_step<kDppBcast15, 0xA>(v);
+  v = umax_step<kDppBcast31, 0xC>(v);
+  return __builtin_amdgcn_readlane(v, 63);
+}
+
+// Sum over the wave in a fixed tree; every lane gets the lane-63 result, so
+// the value is uniform and reproducible from run to run.
+template <int CTRL, int ROWS>
+__device__ __forceinline__ float add_step(float v) {
+  // Lanes outside ROWS receive 0 (old) and keep their value.
+  return v + __uint_as_float(dpp<CTRL, ROWS>(0u, __float_as_uint(v)));
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
-  return v;
+  v = add_step<kDppQuadX1, 0xF>(v);
+  v = add_step<kDppQuadX2, 0xF>(v);
+  v = add_step<kDppHalfMirror, 0xF>(v);
+  v = add_step<kDppMirror, 0xF>(v);
+  v = add_step<kDppBcast15, 0xA>(v);
+  v = add_step<kDppBcast31, 0xC>(v);
+  return __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(v), 63));
+}
+
+template <int CTRL, int ROWS>
+__device__ __forceinline__ float fmax_step(float v) {
+  return fmaxf(v, __uint_as_float(dpp<CTRL, ROWS>(__float_as_uint(v), __float_as_uint(v))));
 }
 
 __device__ __forceinline__ float wave_maxf(float v) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
-  return v;
+  v = fmax_step<kDppQuadX1, 0xF>(v);
+  v = fmax_step<kDppQuadX2, 0xF>(v);
+  v = fmax_step<kDppHalfMirror, 0xF>(v);
+  v = fmax_step<kDppMirror, 0xF>(v);
+  v = fmax_step<kDppBcast15, 0xA>(v);
+  v = fmax_step<kDppBcast31, 0xC>(v);
+  return __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(v), 63));
 }
 
-// Up to `rounds` rounds of wave-wide argmax over the candidate keys. Lane r
-// receives the r-th winner. Returns the number of winners.
-__device__ __forceinline__ int wave_rank(uint64_t (&key)[kNV], int rounds, int lane, int &my_id,
-                                float &my_val, float &first_val) {
+// Up to `rounds` rounds of wave-wide argmax over the keys (expert lane+64v
+// holds key[v]). Lane r receives the r-th winner's expert and key; `top` is
+// the first winner's key. Returns the number of winners.
+template <int NV>
+__device__ __forceinline__ int wave_rank(uint32_t (&key)[NV], int rounds, int lane, int &my_e,
+                                         uint32_t &my_key, uint32_t &top) {
   int n = 0;
   for (int r = 0; r < rounds; ++r) {
-    uint64_t best = key[0];
+    uint32_t best = key[0];
 #pragma unroll
-    for (int v = 1; v < kNV; ++v) best = key[v] > best ? key[v] : best;
-    best = wave_max_u64(best);
+    for (int v = 1; v < NV; ++v) best = key[v] > best ? key[v] : best;
+    best = wave_max_u32(best);
     if (best == 0) break;
-    const int e = int(0xFFFFFFFFu - uint32_t(best));
-    const float val = from_ord_bits(uint32_t(best >> 32));
-    if (lane == r) {
-      my_id = e;
-      my_val = val;
-    }
-    if (r == 0) first_val = val;
+    int e = 0;
 #pragma unroll
-    for (int v = 0; v < kNV; ++v)
+    for (int v = NV - 1; v >= 0; --v) {  // the lowest index holding `best` wins
+      const unsigned long long b = __ballot(key[v] == best);
+      if (b) e = 64 * v + __builtin_ctzll(b);
+    }
+    if (lane == r) {
+      my_e = e;
+      my_key = best;
+    }
+    if (r == 0) top = best;
+#pragma unroll
+    for (int v = 0; v < NV; ++v)
       if (lane + 64 * v == e) key[v] = 0;
     ++n;
   }
@@ -100,6 +148,7 @@ __device__ __forceinline__ int wave_rank(uint64_t (&key)[kNV], int rounds, int l
 
 __device__ __forceinline__ bool bit_of(const uint32_t *mask, int e) { return (mask[e >> 5] >> (e & 31)) & 1u; }
 
+template <int NV>
 __global__ __launch_bounds__(kThreads) void select_kernel(
     const float *__restrict__ logits, int B, int E, int kind, int k, int k0, int m,
     int32_t *__restrict__ topk_ids, float *__restrict__ topk_w, int32_t *__restrict__ n_active,
@@ -107,11 +156,12 @@ __global__ __launch_bounds__(kThreads) void select_kernel(
     int32_t *__restrict__ pair_token, int32_t *__restrict__ pair_slot,
     float *__restrict__ batch_mass) {
   __shared__ uint32_t allowed[kWords];
-  __shared__ uint32_t tokmask[kMaxB][kWords];
-  __shared__ int16_t sel_ids[kMaxB][kMaxK];
+  __shared__ uint32_t etok[kMaxE][kTokWords];  // bit t of etok[e]: token t routes to e
+  __shared__ int16_t sel_id[kMaxB][kMaxK];
+  __shared__ float sel_w[kMaxB][kMaxK];
   __shared__ float psum[kWaves][kMaxE];
   __shared__ float mass[kMaxE];
-  __shared__ int cnt[kMaxE];
+  __shared__ int acnt[kMaxE];
   __shared__ int apos[kMaxE];
   __shared__ int aoff[kMaxE];
   __shared__ int s_n, s_total;
@@ -129,21 +179,20 @@ __global__ __launch_bounds__(kThreads) void select_kernel(
     }
     allowed[i] = full;
   }
-  for (int i = tid; i < B * kWords; i += kThreads) tokmask[i / kWords][i % kWords] = 0;
-  for (int i = tid; i < kMaxE; i += kThreads) cnt[i] = 0;
+  for (int i = tid; i < kMaxE * kTokWords; i += kThreads) etok[i / kTokWords][i % kTokWords] = 0;
 
-  __syncthreads();
-
-  float L[kTokPerWave][kNV];
+  // Phase 1: logits into registers. Addresses are clamped so that every load
+  // is in bounds; values outside [B, E) are never used as candidates.
+  float L[kTokPerWave][NV];
 #pragma unroll
   for (int ti = 0; ti < kTokPerWave; ++ti) {
-    const int t = wave + kWaves * ti;
+    if (ti * kWaves < B) {  // wave-uniform
+      const int t = min(wave + kWaves * ti, B - 1);
 #pragma unroll
-    for (int v = 0; v < kNV; ++v) {
-      const int e = lane + 64 * v;
-      L[ti][v] = (t < B && e < E) ? logits[t * E + e] : 0.0f;
+      for (int v = 0; v < NV; ++v) L[ti][v] = logits[t * E + min(lane + 64 * v, E - 1)];
     }
   }
+  __syncthreads();
 
   // Phase 2: the policy's batch step.
   if (kind == MOE_POLICY_OEA) {
@@ -151,16 +200,13 @@ __global__ __launch_bounds__(kThreads) void select_kernel(
     for (int ti = 0; ti < kTokPerWave; ++ti) {
       const int t = wave + kWaves * ti;
       if (t < B) {
-        uint64_t key[kNV];
+        uint32_t key[NV];
 #pragma unroll
-        for (int v = 0; v < kNV; ++v) {
-          const int e = lane + 64 * v;
-          key[v] = e < E ? make_key(L[ti][v], e) : 0;
-        }
-        int id = -1;
-        float val = 0.0f, first = 0.0f;
-        const int n = wave_rank(key, k0, lane, id, val, first);
-        if (lane < n) atomicOr(&allowed[id >> 5], 1u << (id & 31));
+        for (int v = 0; v < NV; ++v) key[v] = (lane + 64 * v < E) ? ord_bits(L[ti][v]) : 0u;
+        int e = 0;
+        uint32_t kv = 0, top = 0;
+        const int n = wave_rank<NV>(key, k0, lane, e, kv, top);
+        if (lane < n) atomicOr(&allowed[e >> 5], 1u << (e & 31));
       }
     }
   } else if (kind == MOE_POLICY_BUDGET) {
@@ -173,17 +219,17 @@ __global__ __launch_bounds__(kThreads) void select_kernel(
       if (ti < rounds) {  // block-uniform: every wave reaches the same barriers
         const int t = wave + kWaves * ti;
         float mx = -INFINITY;
-  #pragma unroll
-        for (int v = 0; v < kNV; ++v)
+#pragma unroll
+        for (int v = 0; v < NV; ++v)
           if (lane + 64 * v < E) mx = fmaxf(mx, L[ti][v]);
         mx = wave_maxf(mx);
         float sm = 0.0f;
-  #pragma unroll
-        for (int v = 0; v < kNV; ++v)
+#pragma unroll
+        for (int v = 0; v < NV; ++v)
           if (lane + 64 * v < E) sm += expf(L[ti][v] - mx);
         sm = wave_sum(sm);
-  #pragma unroll
-        for (int v = 0; v < kNV; ++v) {
+#pragma unroll
+        for (int v = 0; v < NV; ++v) {
           const int e = lane + 64 * v;
           if (e < E) psum[wave][e] = (t < B) ? expf(L[ti][v] - mx) / sm : 0.0f;
         }
@@ -194,10 +240,7 @@ __global__ __launch_bounds__(kThreads) void select_kernel(
         __syncthreads();
       }
     }
-    if (tid < E) {
-      mass[tid] = macc;
-      if (batch_mass) batch_mass[tid] = macc;
-    }
+    if (tid < E) mass[tid] = macc;
     __syncthreads();
     if (tid < E) {
       int rank = 0;
@@ -215,39 +258,40 @@ __global__ __launch_bounds__(kThreads) void select_kernel(
   for (int ti = 0; ti < kTokPerWave; ++ti) {
     const int t = wave + kWaves * ti;
     if (t < B) {
-      uint64_t key[kNV];
-  #pragma unroll
-      for (int v = 0; v < kNV; ++v) {
+      uint32_t key[NV];
+#pragma unroll
+      for (int v = 0; v < NV; ++v) {
         const int e = lane + 64 * v;
-        key[v] = (e < E && bit_of(allowed, e)) ? make_key(L[ti][v], e) : 0;
+        key[v] = (e < E && bit_of(allowed, e)) ? ord_bits(L[ti][v]) : 0u;
       }
-      int id = -1;
-      float val = 0.0f, first = 0.0f;
-      const int n = wave_rank(key, k, lane, id, val, first);
-      const float ex = lane < n ? expf(val - first) : 0.0f;
+      int e = 0;
+      uint32_t kv = 0, top = 0;
+      const int n = wave_rank<NV>(key, k, lane, e, kv, top);
+      const float ex = lane < n ? expf(from_ord_bits(kv) - from_ord_bits(top)) : 0.0f;
       const float tot = wave_sum(ex);
       if (lane < k) {
-        topk_ids[t * k + lane] = lane < n ? id : -1;
-        topk_w[t * k + lane] = lane < n ? ex / tot : 0.0f;
-        sel_ids[t][lane] = int16_t(lane < n ? id : -1);
+        sel_id[t][lane] = int16_t(lane < n ? e : -1);
+        sel_w[t][lane] = lane < n ? ex / tot : 0.0f;
       }
-      if (lane < n) {
-        atomicOr(&tokmask[t][id >> 5], 1u << (id & 31));
-        atomicAdd(&cnt[id], 1);
-      }
+      if (lane < n) atomicOr(&etok[e][t >> 5], 1u << (t & 31));
     }
   }
   __syncthreads();
 
-  // Phase 4: compaction. Wave 0 scans the per-expert counts.
+  // Phase 4: wave 0 counts each expert's tokens and scans the counts; lane l
+  // owns experts l*NV .. l*NV+NV-1 so that the scan runs in expert order.
   if (wave == 0) {
-    int c[kNV], a[kNV];
+    const int nw = (B + 31) >> 5;
+    int c[NV], a[NV];
     int lc = 0, la = 0;
 #pragma unroll
-    for (int v = 0; v < kNV; ++v) {
-      const int e = lane * kNV + v;
-      c[v] = (e < E) ? cnt[e] : 0;
-      a[v] = c[v] > 0;
+    for (int v = 0; v < NV; ++v) {
+      const int e = lane * NV + v;
+      int cv = 0;
+      if (e < E)
+        for (int w = 0; w < nw; ++w) cv += __popc(etok[e][w]);
+      c[v] = cv;
+      a[v] = cv > 0;
       lc += c[v];
       la += a[v];
     }
@@ -263,9 +307,10 @@ __global__ __launch_bounds__(kThreads) void select_kernel(
     }
     int pc = ic - lc, pa = ia - la;
 #pragma unroll
-    for (int v = 0; v < kNV; ++v) {
-      const int e = lane * kNV + v;
+    for (int v = 0; v < NV; ++v) {
+      const int e = lane * NV + v;
       if (e < E) {
+        acnt[e] = c[v];
         aoff[e] = pc;
         apos[e] = pa;
       }
@@ -279,25 +324,30 @@ __global__ __launch_bounds__(kThreads) void select_kernel(
   }
   __syncthreads();
 
-  const int nact = s_n, total = s_total;
-  if (tid < E && cnt[tid] > 0) {
-    const int e = tid;
-    const int ap = apos[e];
-    int c = aoff[e];
-    active_experts[ap] = e;
-    expert_offsets[ap] = c;
-    for (int t = 0; t < B; ++t) {
-      if (!bit_of(tokmask[t], e)) continue;
-      int j = 0;
-      while (sel_ids[t][j] != e) ++j;
-      pair_token[c] = t;
-      pair_slot[c] = j;
-      ++c;
-    }
+  // Phase 5: every output, written once, by all threads.
+  const int nact = s_n, total = s_total, P = B * k;
+  if (tid < E && acnt[tid] > 0) {
+    active_experts[apos[tid]] = tid;
+    expert_offsets[apos[tid]] = aoff[tid];
   }
+  if (tid < E && batch_mass) batch_mass[tid] = mass[tid];
   for (int i = nact + tid; i < E; i += kThreads) active_experts[i] = -1;
   for (int i = nact + tid; i <= E; i += kThreads) expert_offsets[i] = total;
-  for (int i = total + tid; i < B * k; i += kThreads) {
+  for (int i = tid; i < P; i += kThreads) {
+    const int t = i / k, j = i - t * k;
+    const int e = sel_id[t][j];
+    topk_ids[i] = e;
+    topk_w[i] = sel_w[t][j];
+    if (e >= 0) {
+      const uint32_t *row = etok[e];
+      int pos = aoff[e];
+      for (int w = 0; w < (t >> 5); ++w) pos += __popc(row[w]);
+      pos += __popc(row[t >> 5] & ((1u << (t & 31)) - 1u));
+      pair_token[pos] = t;
+      pair_slot[pos] = j;
+    }
+  }
+  for (int i = total + tid; i < P; i += kThreads) {
     pair_token[i] = -1;
     pair_slot[i] = -1;
   }
@@ -308,9 +358,17 @@ __global__ __launch_bounds__(kThreads) void select_kernel(
 
 hipError_t launch_select(const float *logits, int B, int E, moe_policy_t p,
                          const moe_routing_t &r, hipStream_t s) {
-  select_kernel<<<1, kThreads, 0, s>>>(logits, B, E, p.kind, p.k, p.k0, p.m,
-                                       r.topk_ids, r.topk_w, r.n_active, r.active_experts,
-                                       r.expert_offsets, r.pair_token, r.pair_slot, r.batch_mass);
+  auto go = [&](auto kern) {
+    kern<<<1, kThreads, 0, s>>>(logits, B, E, p.kind, p.k, p.k0, p.m, r.topk_ids, r.topk_w,
+                                r.n_active, r.active_experts, r.expert_offsets, r.pair_token,
+                                r.pair_slot, p.kind == MOE_POLICY_BUDGET ? r.batch_mass : nullptr);
+  };
+  if (E <= 64)
+    go(select_kernel<1>);
+  else if (E <= 128)
+    go(select_kernel<2>);
+  else
+    go(select_kernel<4>);
   return hipGetLastError();
 }
 
