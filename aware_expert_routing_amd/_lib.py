@@ -161,7 +161,8 @@ def alloc_workspace(B: int, d: int, E: int, I: int, k: int, dtype, device="cuda"
     n = moe_workspace_bytes(B, d, E, I, k, dtype)
     if n == 0:
         raise MoeError(MOE_ERR_UNSUPPORTED, status_string(MOE_ERR_UNSUPPORTED))
-    return torch.empty((n,), dtype=torch.uint8, device=device)
+    # Zero-filled once: the expert FFN keeps its grid-barrier words here.
+    return torch.zeros((n,), dtype=torch.uint8, device=device)
 
 
 def moe_route(x, w_g, bias, logits, workspace, stream=None):

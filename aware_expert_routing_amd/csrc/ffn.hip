@@ -91,12 +91,41 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, ui
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, int(bytes), kRsrcWord3);
 }
 
+// Cache-policy bits of a memory instruction: SC1 makes it coherent at device
+// scope (across XCDs), which data exchanged between workgroups of one kernel
+// needs.
+constexpr int kPolicyDevice = 16;
+
 // Copies 16 bytes per lane from buffer offset voff + soff into LDS at
 // dst + 16*lane. Offsets at or past the end of the buffer read as zero.
+template <int POLICY = 0>
 __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, unsigned char *dst, uint32_t voff,
                                       uint32_t soff) {
   // A C-style cast is the way to move a generic pointer into the LDS address space.
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t *)(dst), 16, int(voff), int(soff), 0, 0);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t *)(dst), 16, int(voff), int(soff), 0, POLICY);
+}
+
+// Device-scope stores and loads of data that other workgroups of the same
+// kernel read or wrote (partial sums, h, down rows, the slot map). They reach
+// or come from the device-coherent level directly, so the grid barrier needs
+// no cache write-back or invalidation.
+__device__ __forceinline__ void st_dev(float *p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_dev(int32_t *p, int32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_dev(uint64_t *p, uint64_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_dev(const float *p) {
+  return __hip_atomic_load(const_cast<float *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ int32_t ld_dev(const int32_t *p) {
+  return __hip_atomic_load(const_cast<int32_t *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float4 ld_dev4(const float *p) {
+  return make_float4(ld_dev(p), ld_dev(p + 1), ld_dev(p + 2), ld_dev(p + 3));
 }
 
 // s_waitcnt vmcnt(N) lgkmcnt(0), then s_barrier. Compiler barriers keep LDS
@@ -184,33 +213,89 @@ __device__ __forceinline__ void lds_b128<4>(const uint32_t (&a)[4], bf16x8_t (&x
                : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]));
 }
 
+// Grid-barrier words in the workspace: arrival count, generation, error flag
+// (each on its own 128-byte line). The count is back at zero after every
+// barrier; the generation only grows.
+constexpr int kSyncCount = 0;
+constexpr int kSyncGen = 32;
+constexpr int kSyncErr = 64;
+constexpr uint32_t kSpinLimit = 1u << 20;
+
+// All workgroups of the grid (resident together: one per CU at most) meet
+// here. Every store a workgroup makes before the barrier and that others
+// read after it is a device-scope store, and those reads are device-scope
+// loads, so completing the stores before arriving (s_waitcnt vmcnt(0)) is
+// what orders them before the reads; no cache maintenance is needed. A wait
+// that does not end within kSpinLimit polls sets the error word and returns,
+// so the kernel always terminates.
+__device__ __forceinline__ void grid_barrier(uint32_t *sync) {
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t *count = sync + kSyncCount, *gen = sync + kSyncGen;
+    const uint32_t g0 = __hip_atomic_load(gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // The generation must be read before this workgroup's arrival can let
+    // the last arriver advance it.
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    const uint32_t arrived =
+        __hip_atomic_fetch_add(count, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (arrived == gridDim.x - 1) {
+      __hip_atomic_store(count, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __hip_atomic_fetch_add(gen, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    } else {
+      for (uint32_t n = 0; __hip_atomic_load(gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == g0;
+           ++n) {
+        if (n >= kSpinLimit) {
+          __hip_atomic_store(sync + kSyncErr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+      }
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  }
+  __syncthreads();
+}
+
 struct Params {
-  const uint16_t *A;       // x [B,d] (up) or h [P,I] (down)
-  uint32_t a_bytes;        // size of A in bytes
-  int a_ld;                // row stride of A (elements): d (up) or I (down)
-  const uint16_t *W[2];    // G, U (up) or D (down): [E, K, N]
-  int K, N;                // reduction length and output columns per expert
-  int slices, slice_rows;  // reduction slices per expert
-  int P;                   // pair capacity (B*k)
-  float *out;              // up: float [slices][2][P][N]; down: float [P][N] by pair
+  const uint16_t *x;          // [B, d]
+  const uint16_t *W[3];       // G, U: [E, d, I]; D: [E, I, d]
+  int B, d, I, k;
+  int slices, slice_rows;     // gate/up reduction slices over d
+  int P;                      // B * k
+  float *gpart;               // [slices][2][P][I] gate/up partial sums by pair
+  uint16_t *h;                // [P][I] SiLU(g) * u by pair
+  float *part;                // [P][d] down-projection rows by pair
+  int32_t *pair_of_slot;      // [P] pair index of token slot t*k+j
+  uint16_t *y;                // [B][d]
+  const int32_t *ids;         // [B][k]
+  const float *w;             // [B][k]
+  const int32_t *pair_token;  // [P]
+  const int32_t *pair_slot;   // [P]
+  uint32_t *sync;             // grid-barrier words
 };
 
-// A position in a workgroup's stage sequence. All fields are wave-uniform
-// except arow (the A rows this lane copies).
+// A position in a workgroup's stage sequence. The workgroup's items are
+// b, b+G, b+2G, ... of one list: gate/up items first (expert, 64-column strip
+// of I, slice of d), then down items (expert, 128-column strip of d, all of
+// I). Every stage holds two weight tiles (G and U, or two adjacent 64-column
+// tiles of D) and the A tile of the same reduction rows (x rows gathered by
+// token, or h rows by pair). All fields are wave-uniform.
 struct Cursor {
-  int item, n_items, per_expert;
-  int e, p0, T, strip, ks, row0, nrows, nst, npass;
-  int pass, kst;
-  bool valid;
+  int item, n_items, n_up, per_up, per_dn;
+  int e, p0, T, strip, ks, row0, nrows, nst, npass, pass, kst;
+  bool valid, up;
 };
 
-template <int NMAT, int MTX, bool UP>
+template <int MTX>
 struct Stream {
-  using S = Shape<NMAT, MTX>;
+  using S = Shape<2, MTX>;
   const Params &p;
   uint32_t meta;            // LDS address of the routing lists
   int wave, lane, g, j;
-  uint32_t wvoff[4];        // weight copy offsets (bytes) within a stage, copies w + 4h
+  uint32_t wv_up[4];        // weight copy offsets within a stage (row stride I)
+  uint32_t wv_dn[4];        // the same for D (row stride d)
   uint32_t trc[2];          // transposing-read offsets within a weight tile
   uint32_t xrd;             // A-fragment read offset within a k-step sub-tile
   uint32_t dotrd;           // token-row read offset for the dot2 path
@@ -224,7 +309,8 @@ struct Stream {
     for (int h = 0; h < 4; ++h) {
       const int r = 8 * (wave + 4 * h) + (lane >> 3);
       const int lc = (lane & 7) ^ swz_w(r);
-      wvoff[h] = uint32_t(r) * uint32_t(p.N) * 2u + uint32_t(lc) * 16u;
+      wv_up[h] = uint32_t(r) * uint32_t(p.I) * 2u + uint32_t(lc) * 16u;
+      wv_dn[h] = uint32_t(r) * uint32_t(p.d) * 2u + uint32_t(lc) * 16u;
     }
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
@@ -239,25 +325,36 @@ struct Stream {
   __device__ __forceinline__ void decode(Cursor &c) const {
     c.valid = c.item < c.n_items;
     if (!c.valid) return;
-    const int a = c.item / c.per_expert;
-    const int rem = c.item - a * c.per_expert;
-    c.strip = rem / p.slices;
-    c.ks = rem - c.strip * p.slices;
+    c.up = c.item < c.n_up;
+    int a;
+    if (c.up) {
+      a = c.item / c.per_up;
+      const int rem = c.item - a * c.per_up;
+      c.strip = rem / p.slices;
+      c.ks = rem - c.strip * p.slices;
+      c.row0 = c.ks * p.slice_rows;
+      c.nrows = min(p.slice_rows, p.d - c.row0);
+    } else {
+      const int jd = c.item - c.n_up;
+      a = jd / c.per_dn;
+      c.strip = jd - a * c.per_dn;
+      c.ks = 0;
+      c.row0 = 0;
+      c.nrows = p.I;
+    }
     c.e = __builtin_amdgcn_readfirstlane(lds_i16(meta + kMetaAct + 2 * a));
     c.p0 = __builtin_amdgcn_readfirstlane(lds_i16(meta + kMetaOff + 2 * a));
     c.T = __builtin_amdgcn_readfirstlane(lds_i16(meta + kMetaOff + 2 * a + 2)) - c.p0;
-    c.row0 = c.ks * p.slice_rows;
-    c.nrows = min(p.slice_rows, p.K - c.row0);
     c.nst = (c.nrows + kBK - 1) / kBK;
     c.npass = (c.T + kMaxTok - 1) / kMaxTok;
     c.pass = 0;
     c.kst = 0;
   }
-  __device__ __forceinline__ void advance(Cursor &c, int stride) const {
+  __device__ __forceinline__ void advance(Cursor &c) const {
     if (++c.kst < c.nst) return;
     c.kst = 0;
     if (++c.pass < c.npass) return;
-    c.item += stride;
+    c.item += gridDim.x;
     decode(c);
   }
   __device__ __forceinline__ static int tp(const Cursor &c) { return min(kMaxTok, c.T - c.pass * kMaxTok); }
@@ -268,40 +365,66 @@ struct Stream {
     const int m = 16 * h + (lane >> 2);
     const int T = tp(c);
     const int pr = c.p0 + c.pass * kMaxTok + (m < T ? m : T - 1);
-    const int arow = UP ? lds_u8(meta + kMetaTok + pr) : pr;
     const int lc = (lane & 3) ^ swz_x(m);
-    return (uint32_t(arow) * uint32_t(p.a_ld) + uint32_t(wave * 32 + lc * 8)) * 2u;
+    const uint32_t kofs = uint32_t(wave * 32 + lc * 8);
+    if (c.up) return (uint32_t(lds_u8(meta + kMetaTok + pr)) * uint32_t(p.d) + kofs) * 2u;
+    return (uint32_t(pr) * uint32_t(p.I) + kofs) * 2u;
   }
 
-  // Issues the copies of stage c into `slot` (S::kCopies per wave).
-  __device__ __forceinline__ void issue(const Cursor &c, unsigned char *slot) const {
-    const size_t base = (size_t(c.e) * p.K + c.row0) * p.N;
-    const uint32_t wbytes = uint32_t(c.nrows) * uint32_t(p.N) * 2u;
-    const uint32_t soff = (uint32_t(c.kst * kBK) * uint32_t(p.N) + uint32_t(c.strip * kStripCols)) * 2u;
-#pragma unroll
-    for (int mat = 0; mat < NMAT; ++mat) {
-      const __amdgpu_buffer_rsrc_t r = make_rsrc(p.W[mat] + base, wbytes);
-#pragma unroll
-      for (int h = 0; h < 4; ++h) dma16(r, slot + mat * kWTile + (wave + 4 * h) * 1024, wvoff[h], soff);
-    }
-    const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.A, p.a_bytes);
+  // The A-tile copies of stage c (MTX per wave). A down stage issued before
+  // h exists (h_ok false) copies x instead, a harmless stand-in that keeps
+  // the number of copies per stage fixed; its A tile is copied again once h
+  // is complete. h is read with device-scope copies (other workgroups wrote it).
+  __device__ __forceinline__ void issue_a(const Cursor &c, unsigned char *slot, bool h_ok) const {
+    unsigned char *dst = slot + 2 * kWTile + wave * S::kXSub;
     const uint32_t xsoff = uint32_t(c.row0 + c.kst * kBK) * 2u;
+    if (c.up || !h_ok) {
+      const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.x, uint32_t(p.B) * uint32_t(p.d) * 2u);
 #pragma unroll
-    for (int h = 0; h < MTX; ++h)
-      dma16(ra, slot + NMAT * kWTile + wave * S::kXSub + h * 1024, xvoff(c, h), xsoff);
+      for (int h = 0; h < MTX; ++h) dma16(ra, dst + h * 1024, c.up ? xvoff(c, h) : uint32_t(lane * 16), c.up ? xsoff : 0u);
+    } else {
+      const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.h, uint32_t(p.P) * uint32_t(p.I) * 2u);
+#pragma unroll
+      for (int h = 0; h < MTX; ++h) dma16<kPolicyDevice>(ra, dst + h * 1024, xvoff(c, h), xsoff);
+    }
+  }
+
+  // Issues every copy of stage c into `slot` (S::kCopies per wave).
+  __device__ __forceinline__ void issue(const Cursor &c, unsigned char *slot, bool h_ok) const {
+    if (c.up) {
+      const size_t base = (size_t(c.e) * p.d + c.row0) * p.I;
+      const uint32_t wbytes = uint32_t(c.nrows) * uint32_t(p.I) * 2u;
+      const uint32_t soff =
+          (uint32_t(c.kst * kBK) * uint32_t(p.I) + uint32_t(c.strip * kStripCols)) * 2u;
+#pragma unroll
+      for (int mat = 0; mat < 2; ++mat) {
+        const __amdgpu_buffer_rsrc_t r = make_rsrc(p.W[mat] + base, wbytes);
+#pragma unroll
+        for (int h = 0; h < 4; ++h) dma16(r, slot + mat * kWTile + (wave + 4 * h) * 1024, wv_up[h], soff);
+      }
+    } else {
+      const size_t base = size_t(c.e) * p.I * p.d;
+      const __amdgpu_buffer_rsrc_t r = make_rsrc(p.W[2] + base, uint32_t(p.I) * uint32_t(p.d) * 2u);
+#pragma unroll
+      for (int mat = 0; mat < 2; ++mat) {
+        const uint32_t soff = (uint32_t(c.kst * kBK) * uint32_t(p.d) +
+                               uint32_t((2 * c.strip + mat) * kStripCols)) * 2u;
+#pragma unroll
+        for (int h = 0; h < 4; ++h) dma16(r, slot + mat * kWTile + (wave + 4 * h) * 1024, wv_dn[h], soff);
+      }
+    }
+    issue_a(c, slot, h_ok);
   }
 };
 
-template <int NMAT>
 struct Acc {
-  f32x4_t mf[NMAT][4];        // MFMA: rows 4*(lane/16)+i of tile mt, column 16*wave + lane%16
-  float dot[NMAT][kDotMaxT];  // dot2: token m over this lane's k-groups
+  f32x4_t mf[2][4];        // MFMA: rows 4*(lane/16)+i of tile mt, column 16*wave + lane%16
+  float dot[2][kDotMaxT];  // dot2: token m over this lane's k-groups
 };
 
-template <int NMAT>
-__device__ __forceinline__ void clear(Acc<NMAT> &acc) {
+__device__ __forceinline__ void clear(Acc &acc) {
 #pragma unroll
-  for (int mat = 0; mat < NMAT; ++mat) {
+  for (int mat = 0; mat < 2; ++mat) {
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) acc.mf[mat][mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -310,49 +433,45 @@ __device__ __forceinline__ void clear(Acc<NMAT> &acc) {
 }
 
 // B fragments of k-step ks for this lane: column 16*wave + j, rows
-// 32ks + 8g .. 32ks + 8g + 7 of each weight tile. The transposing read gives
+// 32ks + 8g .. 32ks + 8g + 7 of both weight tiles. The transposing read gives
 // lane j of a 16-lane group element j of the four rows its group's lanes point
 // at (lane 4r+q points at row r, columns 4q..4q+3).
-template <int NMAT>
 __device__ __forceinline__ void b_frags(uint32_t slot, const uint32_t (&trc)[2], int ks,
                                         bf16x8_t (&b)[2]) {
   const uint32_t o = slot + uint32_t(ks * 32 * kRowBytes);
-  if (NMAT == 2)
-    lds_tr4(o + trc[0], o + trc[1], o + kWTile + trc[0], o + kWTile + trc[1], b[0], b[1]);
-  else
-    lds_tr2(o + trc[0], o + trc[1], b[0]);
+  lds_tr4(o + trc[0], o + trc[1], o + kWTile + trc[0], o + kWTile + trc[1], b[0], b[1]);
 }
 
-template <int NMAT, int MTX, int NA>
+template <int MTX, int NA>
 __device__ __forceinline__ void mfma_stage(uint32_t slot, uint32_t xslot, const uint32_t (&trc)[2],
-                                           uint32_t xrd, Acc<NMAT> &acc) {
+                                           uint32_t xrd, Acc &acc) {
 #pragma unroll
   for (int ks = 0; ks < kKSteps; ++ks) {
     bf16x8_t b[2];
-    b_frags<NMAT>(slot, trc, ks, b);
+    b_frags(slot, trc, ks, b);
     uint32_t aa[4];
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) aa[mt] = xslot + uint32_t(ks * Shape<NMAT, MTX>::kXSub + mt * 1024) + xrd;
+    for (int mt = 0; mt < 4; ++mt) aa[mt] = xslot + uint32_t(ks * Shape<2, MTX>::kXSub + mt * 1024) + xrd;
     bf16x8_t a[4];
     lds_b128<NA>(aa, a);
 #pragma unroll
     for (int mt = 0; mt < NA; ++mt)
 #pragma unroll
-      for (int mat = 0; mat < NMAT; ++mat)
+      for (int mat = 0; mat < 2; ++mat)
         acc.mf[mat][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[mt], b[mat], acc.mf[mat][mt], 0, 0, 0);
   }
 }
 
-template <int NMAT, int MTX>
+template <int MTX>
 __device__ __forceinline__ void dot_stage(uint32_t slot, uint32_t xslot, const uint32_t (&trc)[2],
-                                          uint32_t dotrd, int T, Acc<NMAT> &acc) {
+                                          uint32_t dotrd, int T, Acc &acc) {
 #pragma unroll
   for (int ks = 0; ks < kKSteps; ++ks) {
     bf16x8_t b[2];
-    b_frags<NMAT>(slot, trc, ks, b);
+    b_frags(slot, trc, ks, b);
     // Rows 0..3 of the k-step's A sub-tile: token m's 8 values of this lane's
     // k-group (rows below 4 are not swizzled).
-    const uint32_t xb = xslot + uint32_t(ks * Shape<NMAT, MTX>::kXSub) + dotrd;
+    const uint32_t xb = xslot + uint32_t(ks * Shape<2, MTX>::kXSub) + dotrd;
     const uint32_t aa[4] = {xb, xb + 64, xb + 128, xb + 192};
     bf16x8_t a[4];
     lds_b128<4>(aa, a);
@@ -360,7 +479,7 @@ __device__ __forceinline__ void dot_stage(uint32_t slot, uint32_t xslot, const u
     for (int m = 0; m < kDotMaxT; ++m) {
       if (m < T) {
 #pragma unroll
-        for (int mat = 0; mat < NMAT; ++mat) {
+        for (int mat = 0; mat < 2; ++mat) {
           float s = acc.dot[mat][m];
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
@@ -378,34 +497,47 @@ __device__ __forceinline__ void dot_stage(uint32_t slot, uint32_t xslot, const u
   }
 }
 
-template <int NMAT, int MTX>
+template <int MTX>
 __device__ __forceinline__ void compute_stage(uint32_t slot, const uint32_t (&trc)[2], uint32_t xrd,
-                                              uint32_t dotrd, int T, Acc<NMAT> &acc) {
-  const uint32_t xslot = slot + NMAT * kWTile;
+                                              uint32_t dotrd, int T, Acc &acc) {
+  const uint32_t xslot = slot + 2 * kWTile;
   if (T <= kDotMaxT) {
-    dot_stage<NMAT, MTX>(slot, xslot, trc, dotrd, T, acc);
+    dot_stage<MTX>(slot, xslot, trc, dotrd, T, acc);
     return;
   }
   const int na = (T + 15) >> 4;
-  if (MTX == 1 || na == 1) mfma_stage<NMAT, MTX, 1>(slot, xslot, trc, xrd, acc);
-  else if (MTX == 2 || na == 2) mfma_stage<NMAT, MTX, (MTX >= 2 ? 2 : 1)>(slot, xslot, trc, xrd, acc);
-  else if (na == 3) mfma_stage<NMAT, MTX, (MTX >= 3 ? 3 : 1)>(slot, xslot, trc, xrd, acc);
-  else mfma_stage<NMAT, MTX, (MTX >= 4 ? 4 : 1)>(slot, xslot, trc, xrd, acc);
+  if (MTX == 1 || na == 1) mfma_stage<MTX, 1>(slot, xslot, trc, xrd, acc);
+  else if (MTX == 2 || na == 2) mfma_stage<MTX, (MTX >= 2 ? 2 : 1)>(slot, xslot, trc, xrd, acc);
+  else if (na == 3) mfma_stage<MTX, (MTX >= 3 ? 3 : 1)>(slot, xslot, trc, xrd, acc);
+  else mfma_stage<MTX, (MTX >= 4 ? 4 : 1)>(slot, xslot, trc, xrd, acc);
 }
 
-// Stores the accumulators of the pass that just ended, by pair: up writes
-// gate and up partial sums of slice ks, down the pair's output row.
-template <int NMAT, bool UP>
+// Stores the accumulators of the pass that just ended, by pair: the gate and
+// up partial sums of slice ks, or two 64-column tiles of the down projection.
+// A pass has at most 16 * MTX tokens.
+template <int MTX>
 __device__ __forceinline__ void epilogue(const Cursor &c, const Params &p, int wave, int lane,
-                                         Acc<NMAT> &acc) {
+                                         Acc &acc) {
   const int g = lane >> 4, j = lane & 15;
   const int T = min(kMaxTok, c.T - c.pass * kMaxTok);
-  const int col = c.strip * kStripCols + 16 * wave + j;
   const int pbase = c.p0 + c.pass * kMaxTok;
-  auto row = [&](int mat, int pr) { return UP ? size_t(c.ks * 2 + mat) * p.P + pr : size_t(pr); };
+  float *dst0, *dst1;
+  int col0, col1, ld;
+  if (c.up) {
+    ld = p.I;
+    col0 = col1 = c.strip * kStripCols + 16 * wave + j;
+    dst0 = p.gpart + size_t(c.ks * 2) * p.P * p.I;
+    dst1 = dst0 + size_t(p.P) * p.I;
+  } else {
+    ld = p.d;
+    col0 = 2 * c.strip * kStripCols + 16 * wave + j;
+    col1 = col0 + kStripCols;
+    dst0 = dst1 = p.part;
+  }
+  const bool ok0 = col0 < ld, ok1 = col1 < ld;
   if (T <= kDotMaxT) {
 #pragma unroll
-    for (int mat = 0; mat < NMAT; ++mat)
+    for (int mat = 0; mat < 2; ++mat)
 #pragma unroll
       for (int m = 0; m < kDotMaxT; ++m) {
         float v = acc.dot[mat][m];
@@ -413,32 +545,122 @@ __device__ __forceinline__ void epilogue(const Cursor &c, const Params &p, int w
         v += __shfl_xor(v, 32);
         acc.dot[mat][m] = v;
       }
-    if (g == 0 && col < p.N) {
+    if (g == 0) {
 #pragma unroll
       for (int m = 0; m < kDotMaxT; ++m)
-        if (m < T)
-#pragma unroll
-          for (int mat = 0; mat < NMAT; ++mat) p.out[row(mat, pbase + m) * p.N + col] = acc.dot[mat][m];
+        if (m < T) {
+          const size_t row = size_t(pbase + m) * ld;
+          if (ok0) st_dev(dst0 + row + col0, acc.dot[0][m]);
+          if (ok1) st_dev(dst1 + row + col1, acc.dot[1][m]);
+        }
     }
     return;
   }
-  if (col >= p.N) return;
 #pragma unroll
-  for (int t4 = 0; t4 < 4; ++t4)
+  for (int t4 = 0; t4 < MTX; ++t4)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int m = 16 * t4 + 4 * g + i;
-      if (m < T)
-#pragma unroll
-        for (int mat = 0; mat < NMAT; ++mat) p.out[row(mat, pbase + m) * p.N + col] = acc.mf[mat][t4][i];
+      if (m < T) {
+        const size_t row = size_t(pbase + m) * ld;
+        if (ok0) st_dev(dst0 + row + col0, acc.mf[0][t4][i]);
+        if (ok1) st_dev(dst1 + row + col1, acc.mf[1][t4][i]);
+      }
     }
 }
 
-template <int NMAT, int MTX, bool UP>
-__global__ __launch_bounds__(kThreads, 1) void stream_kernel(
-    Params p, const int32_t *__restrict__ n_active, const int32_t *__restrict__ active,
-    const int32_t *__restrict__ offsets, const int32_t *__restrict__ pair_token) {
-  using S = Shape<NMAT, MTX>;
+// h = SiLU(g) * u from the slice partial sums, spread over the whole grid;
+// also the pair index of every token slot, for the combine. All loads of a
+// thread are issued before the first is used.
+__device__ __forceinline__ void h_phase(const Params &p, int total) {
+  const int q4 = p.I / 4;
+  const int n = total * q4;
+  for (int idx = blockIdx.x * kThreads + threadIdx.x; idx < n; idx += gridDim.x * kThreads) {
+    const int pr = idx / q4;
+    const int c = (idx - pr * q4) * 4;
+    float4 gv[kUpMaxSlices], uv[kUpMaxSlices];
+#pragma unroll
+    for (int s = 0; s < kUpMaxSlices; ++s) {
+      if (s < p.slices) {
+        gv[s] = ld_dev4(p.gpart + ((size_t(s) * 2 + 0) * p.P + pr) * p.I + c);
+        uv[s] = ld_dev4(p.gpart + ((size_t(s) * 2 + 1) * p.P + pr) * p.I + c);
+      }
+    }
+    if (c == 0) st_dev(p.pair_of_slot + p.pair_token[pr] * p.k + p.pair_slot[pr], pr);
+    float4 g = make_float4(0, 0, 0, 0), u = make_float4(0, 0, 0, 0);
+#pragma unroll
+    for (int s = 0; s < kUpMaxSlices; ++s) {
+      if (s < p.slices) {
+        g.x += gv[s].x; g.y += gv[s].y; g.z += gv[s].z; g.w += gv[s].w;
+        u.x += uv[s].x; u.y += uv[s].y; u.z += uv[s].z; u.w += uv[s].w;
+      }
+    }
+    const uint64_t o = uint64_t(f32_to_bf16(silu(g.x) * u.x)) |
+                       (uint64_t(f32_to_bf16(silu(g.y) * u.y)) << 16) |
+                       (uint64_t(f32_to_bf16(silu(g.z) * u.z)) << 32) |
+                       (uint64_t(f32_to_bf16(silu(g.w) * u.w)) << 48);
+    st_dev(reinterpret_cast<uint64_t *>(p.h + size_t(pr) * p.I + c), o);
+  }
+}
+
+// y[t] = sum over slots j in order of w[t,j] * part[pair of (t,j)] (empty
+// slots skipped), spread over the whole grid. A thread first loads its
+// token's slot lists, then every part row it needs, then sums.
+__device__ __forceinline__ void combine_phase(const Params &p) {
+  const int q4 = p.d / 4;
+  const int n = p.B * q4;
+  for (int idx = blockIdx.x * kThreads + threadIdx.x; idx < n; idx += gridDim.x * kThreads) {
+    const int t = idx / q4;
+    const int c = (idx - t * q4) * 4;
+    int pos[kMaxK];
+    float w[kMaxK];
+#pragma unroll
+    for (int j = 0; j < kMaxK; ++j) {
+      pos[j] = -1;
+      w[j] = 0.f;
+      if (j < p.k && p.ids[t * p.k + j] >= 0) {
+        pos[j] = ld_dev(p.pair_of_slot + t * p.k + j);
+        w[j] = p.w[t * p.k + j];
+      }
+    }
+    float4 v[kMaxK];
+#pragma unroll
+    for (int j = 0; j < kMaxK; ++j)
+      if (pos[j] >= 0) v[j] = ld_dev4(p.part + size_t(pos[j]) * p.d + c);
+    float4 acc = make_float4(0, 0, 0, 0);
+#pragma unroll
+    for (int j = 0; j < kMaxK; ++j) {
+      if (pos[j] >= 0) {
+        acc.x = fmaf(w[j], v[j].x, acc.x);
+        acc.y = fmaf(w[j], v[j].y, acc.y);
+        acc.z = fmaf(w[j], v[j].z, acc.z);
+        acc.w = fmaf(w[j], v[j].w, acc.w);
+      }
+    }
+    ushort4 o;
+    o.x = f32_to_bf16(acc.x);
+    o.y = f32_to_bf16(acc.y);
+    o.z = f32_to_bf16(acc.z);
+    o.w = f32_to_bf16(acc.w);
+    *reinterpret_cast<ushort4 *>(p.y + size_t(t) * p.d + c) = o;
+  }
+}
+
+// The whole bf16 expert FFN in one persistent kernel (one workgroup per CU,
+// all resident together):
+//   1. gate/up items stream G and U and store slice partial sums;
+//   2. grid barrier; h = SiLU(g) * u over the grid; grid barrier;
+//   3. down items stream D with h as the A operand and store rows by pair;
+//   4. grid barrier; weighted combine over the grid.
+// The ring keeps copying across phases: the first down stages' weights are in
+// flight while the workgroup waits at the barriers; their A tiles are copied
+// once h is complete.
+template <int MTX>
+__global__ __launch_bounds__(kThreads, 1) void ffn_kernel(Params p,
+                                                          const int32_t *__restrict__ n_active,
+                                                          const int32_t *__restrict__ active,
+                                                          const int32_t *__restrict__ offsets) {
+  using S = Shape<2, MTX>;
   constexpr int kS = S::kStages;
   constexpr int kD = kS - 1;  // stages in flight ahead of the one in use
   __shared__ __attribute__((aligned(1024))) unsigned char lds[kS * S::kSlot + kMetaBytes];
@@ -451,116 +673,86 @@ __global__ __launch_bounds__(kThreads, 1) void stream_kernel(
     reinterpret_cast<int16_t *>(meta + kMetaOff)[i] = int16_t(offsets[i]);
     if (i < nact) reinterpret_cast<int16_t *>(meta + kMetaAct)[i] = int16_t(active[i]);
   }
-  for (int i = threadIdx.x; i < total; i += kThreads) meta[kMetaTok + i] = uint8_t(pair_token[i]);
+  for (int i = threadIdx.x; i < total; i += kThreads) meta[kMetaTok + i] = uint8_t(p.pair_token[i]);
   __syncthreads();
 
-  const Stream<NMAT, MTX, UP> st(p, lds_addr(meta));
+  const Stream<MTX> st(p, lds_addr(meta));
   Cursor cons;
-  cons.per_expert = ((p.N + kStripCols - 1) / kStripCols) * p.slices;
-  cons.n_items = nact * cons.per_expert;
+  cons.per_up = ((p.I + kStripCols - 1) / kStripCols) * p.slices;
+  cons.per_dn = (p.d + 2 * kStripCols - 1) / (2 * kStripCols);
+  cons.n_up = nact * cons.per_up;
+  cons.n_items = cons.n_up + nact * cons.per_dn;
   cons.item = blockIdx.x;
   st.decode(cons);
-  if (!cons.valid) return;
   Cursor prod = cons;
 
   // Prologue: kD stages in flight. `issued` counts the stages issued so far.
   int issued = 0;
   for (int s = 0; s < kD; ++s) {
     if (!prod.valid) break;
-    st.issue(prod, stages + s * S::kSlot);
+    st.issue(prod, stages + s * S::kSlot, false);
     ++issued;
-    st.advance(prod, gridDim.x);
+    st.advance(prod);
   }
 
-  Acc<NMAT> acc;
+  Acc acc;
   clear(acc);
   const uint32_t base = lds_addr(stages);
+  bool h_ready = false;
   for (int s = 0; cons.valid; ++s) {
+    if (!cons.up && !h_ready) {
+      // This workgroup's gate/up stages are all done. The down stages already
+      // in the ring hold stand-in A tiles: copy their h rows now.
+      grid_barrier(p.sync);
+      h_phase(p, total);
+      grid_barrier(p.sync);
+      h_ready = true;
+      Cursor q = cons;
+      for (int t = s; t < issued; ++t) {
+        st.issue_a(q, stages + (t % kS) * S::kSlot, true);
+        st.advance(q);
+      }
+      wait_barrier<0>();
+    }
     // Stage s must have landed; the stages issued after it may stay in flight
     // (S::kCopies copies per wave each).
     const int newer = issued - s - 1;
     switch (newer < kD - 1 ? newer : kD - 1) {
       case 0: wait_barrier<0>(); break;
       case 1: wait_barrier<1 * S::kCopies>(); break;
-      case 2: wait_barrier<2 * S::kCopies>(); break;
-      case 3: wait_barrier<(kD - 1 >= 3 ? 3 : 0) * S::kCopies>(); break;
-      case 4: wait_barrier<(kD - 1 >= 4 ? 4 : 0) * S::kCopies>(); break;
-      default: wait_barrier<(kD - 1 >= 5 ? 5 : 0) * S::kCopies>(); break;
+      case 2: wait_barrier<(kD - 1 >= 2 ? 2 : 0) * S::kCopies>(); break;
+      default: wait_barrier<(kD - 1 >= 3 ? 3 : 0) * S::kCopies>(); break;
     }
     // Every wave is past stage s-1, so its slot takes stage s+kD.
     if (prod.valid) {
-      st.issue(prod, stages + ((s + kD) % kS) * S::kSlot);
+      st.issue(prod, stages + ((s + kD) % kS) * S::kSlot, h_ready);
       ++issued;
-      st.advance(prod, gridDim.x);
+      st.advance(prod);
     }
-    compute_stage<NMAT, MTX>(base + uint32_t((s % kS) * S::kSlot), st.trc, st.xrd, st.dotrd,
-                             st.tp(cons), acc);
+    compute_stage<MTX>(base + uint32_t((s % kS) * S::kSlot), st.trc, st.xrd, st.dotrd, st.tp(cons), acc);
     if (cons.kst == cons.nst - 1) {
-      epilogue<NMAT, UP>(cons, p, st.wave, st.lane, acc);
+      epilogue<MTX>(cons, p, st.wave, st.lane, acc);
       clear(acc);
     }
-    st.advance(cons, gridDim.x);
+    st.advance(cons);
   }
-}
-
-// -------------------------------------------------------------------- h
-// One thread per 4 consecutive columns of one pair. The thread of column 0
-// also records the pair index of the pair's (token, slot), for the combine.
-__global__ __launch_bounds__(kThreads) void h_kernel(const float *__restrict__ gpart, int nks,
-                                                     int P, int I, int k,
-                                                     const int32_t *__restrict__ n_active,
-                                                     const int32_t *__restrict__ offsets,
-                                                     const int32_t *__restrict__ pair_token,
-                                                     const int32_t *__restrict__ pair_slot,
-                                                     uint16_t *__restrict__ h,
-                                                     int32_t *__restrict__ pair_of_slot) {
-  const int total = offsets[n_active[0]];
-  const int q4 = I / 4;
-  const int idx = blockIdx.x * kThreads + threadIdx.x;
-  if (idx >= total * q4) return;
-  const int pr = idx / q4;
-  const int c = (idx - pr * q4) * 4;
-  if (c == 0) pair_of_slot[pair_token[pr] * k + pair_slot[pr]] = pr;
-  float4 g = make_float4(0, 0, 0, 0), u = make_float4(0, 0, 0, 0);
-  for (int s = 0; s < nks; ++s) {
-    const float4 gv = *reinterpret_cast<const float4 *>(gpart + ((size_t(s) * 2 + 0) * P + pr) * I + c);
-    const float4 uv = *reinterpret_cast<const float4 *>(gpart + ((size_t(s) * 2 + 1) * P + pr) * I + c);
-    g.x += gv.x; g.y += gv.y; g.z += gv.z; g.w += gv.w;
-    u.x += uv.x; u.y += uv.y; u.z += uv.z; u.w += uv.w;
+  if (!h_ready) {
+    grid_barrier(p.sync);
+    h_phase(p, total);
+    grid_barrier(p.sync);
   }
-  ushort4 o;
-  o.x = f32_to_bf16(silu(g.x) * u.x);
-  o.y = f32_to_bf16(silu(g.y) * u.y);
-  o.z = f32_to_bf16(silu(g.z) * u.z);
-  o.w = f32_to_bf16(silu(g.w) * u.w);
-  *reinterpret_cast<ushort4 *>(h + size_t(pr) * I + c) = o;
+  grid_barrier(p.sync);
+  combine_phase(p);
 }
 
-// -------------------------------------------------------------- combine
-template <typename OutT>
-__device__ __forceinline__ void store4(OutT *y, float4 v);
-template <>
-__device__ __forceinline__ void store4<uint16_t>(uint16_t *y, float4 v) {
-  ushort4 o;
-  o.x = f32_to_bf16(v.x);
-  o.y = f32_to_bf16(v.y);
-  o.z = f32_to_bf16(v.z);
-  o.w = f32_to_bf16(v.w);
-  *reinterpret_cast<ushort4 *>(y) = o;
-}
-template <>
-__device__ __forceinline__ void store4<float>(float *y, float4 v) {
-  *reinterpret_cast<float4 *>(y) = v;
-}
-
+// ------------------------------------------------------------- combine (f32)
 // y[t] = sum over slots j in order of w[t,j] * part[pair of (t,j)] (empty
 // slots skipped).
-template <typename OutT>
-__global__ __launch_bounds__(kThreads) void combine_kernel(const float *__restrict__ part,
-                                                           const int32_t *__restrict__ pair_of_slot,
-                                                           const int32_t *__restrict__ topk_ids,
-                                                           const float *__restrict__ topk_w,
-                                                           int B, int d, int k, OutT *__restrict__ y) {
+__global__ __launch_bounds__(kThreads) void combine_f32_kernel(const float *__restrict__ part,
+                                                               const int32_t *__restrict__ pair_of_slot,
+                                                               const int32_t *__restrict__ topk_ids,
+                                                               const float *__restrict__ topk_w,
+                                                               int B, int d, int k, float *__restrict__ y) {
   const int q4 = d / 4;
   const int idx = blockIdx.x * kThreads + threadIdx.x;
   if (idx >= B * q4) return;
@@ -576,7 +768,7 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const float *__restri
     acc.z = fmaf(w, v.z, acc.z);
     acc.w = fmaf(w, v.w, acc.w);
   }
-  store4<OutT>(y + size_t(t) * d + c, acc);
+  *reinterpret_cast<float4 *>(y + size_t(t) * d + c) = acc;
 }
 
 // ----------------------------------------------------------- float32 path
@@ -636,22 +828,9 @@ int device_cus() {
   return cus;
 }
 
-template <int NMAT, bool UP>
-void launch_stream(int mtx, int grid, const Params &p, const moe_routing_t &r, hipStream_t s) {
-  switch (mtx) {
-    case 1:
-      stream_kernel<NMAT, 1, UP><<<grid, kThreads, 0, s>>>(p, r.n_active, r.active_experts,
-                                                         r.expert_offsets, r.pair_token);
-      break;
-    case 2:
-      stream_kernel<NMAT, 2, UP><<<grid, kThreads, 0, s>>>(p, r.n_active, r.active_experts,
-                                                         r.expert_offsets, r.pair_token);
-      break;
-    default:
-      stream_kernel<NMAT, 4, UP><<<grid, kThreads, 0, s>>>(p, r.n_active, r.active_experts,
-                                                         r.expert_offsets, r.pair_token);
-      break;
-  }
+template <int MTX>
+void launch_ffn(int grid, const Params &p, const moe_routing_t &r, hipStream_t s) {
+  ffn_kernel<MTX><<<grid, kThreads, 0, s>>>(p, r.n_active, r.active_experts, r.expert_offsets);
 }
 
 }  // namespace
@@ -665,48 +844,41 @@ hipError_t launch_expert_ffn(const void *x, const void *w_gate, const void *w_up
   float *part = reinterpret_cast<float *>(ws + plan.down_part);
   int32_t *pos = reinterpret_cast<int32_t *>(ws + plan.pair_of_slot);
   if (dt == MOE_BF16) {
-    float *gpart = reinterpret_cast<float *>(ws + plan.up_part);
-    uint16_t *h = reinterpret_cast<uint16_t *>(ws + plan.h);
+    Params p{};
+    p.x = static_cast<const uint16_t *>(x);
+    p.W[0] = static_cast<const uint16_t *>(w_gate);
+    p.W[1] = static_cast<const uint16_t *>(w_up);
+    p.W[2] = static_cast<const uint16_t *>(w_down);
+    p.B = B;
+    p.d = d;
+    p.I = I;
+    p.k = k;
+    p.slices = plan.up_slices;
+    p.slice_rows = plan.up_slice_rows;
+    p.P = P;
+    p.gpart = reinterpret_cast<float *>(ws + plan.up_part);
+    p.h = reinterpret_cast<uint16_t *>(ws + plan.h);
+    p.part = part;
+    p.pair_of_slot = pos;
+    p.y = static_cast<uint16_t *>(y);
+    p.ids = r.topk_ids;
+    p.w = r.topk_w;
+    p.pair_token = r.pair_token;
+    p.pair_slot = r.pair_slot;
+    p.sync = reinterpret_cast<uint32_t *>(ws + plan.sync);
+    // One workgroup per CU at most, so that the whole grid is resident and
+    // the grid barriers cannot wait on a workgroup that has not started.
+    const int items = max_active * (ceil_div(I, kStripCols) * plan.up_slices + ceil_div(d, 2 * kStripCols));
     const int cus = device_cus();
-    // An expert has at most B tokens: A tiles of 16 * mtx rows cover them
+    const int grid = items < cus ? items : cus;
+    // An expert has at most B tokens: A tiles of 16 * MTX rows cover them
     // (experts with more than 64 tokens take several passes).
-    const int mtx = B <= 16 ? 1 : B <= 32 ? 2 : 4;
-
-    Params up{};
-    up.A = static_cast<const uint16_t *>(x);
-    up.a_bytes = uint32_t(size_t(B) * d * 2);
-    up.a_ld = d;
-    up.W[0] = static_cast<const uint16_t *>(w_gate);
-    up.W[1] = static_cast<const uint16_t *>(w_up);
-    up.K = d;
-    up.N = I;
-    up.slices = plan.up_slices;
-    up.slice_rows = plan.up_slice_rows;
-    up.P = P;
-    up.out = gpart;
-    const int up_items = max_active * ceil_div(I, kStripCols) * plan.up_slices;
-    launch_stream<2, true>(mtx, up_items < cus ? up_items : cus, up, r, s);
-
-    h_kernel<<<ceil_div(P * (I / 4), kThreads), kThreads, 0, s>>>(
-        gpart, plan.up_slices, P, I, k, r.n_active, r.expert_offsets, r.pair_token, r.pair_slot, h,
-        pos);
-
-    Params dn = up;
-    dn.A = h;
-    dn.a_bytes = uint32_t(size_t(P) * I * 2);
-    dn.a_ld = I;
-    dn.W[0] = static_cast<const uint16_t *>(w_down);
-    dn.W[1] = nullptr;
-    dn.K = I;
-    dn.N = d;
-    dn.slices = 1;
-    dn.slice_rows = I;
-    dn.out = part;
-    const int down_items = max_active * ceil_div(d, kStripCols);
-    launch_stream<1, false>(mtx, down_items < cus ? down_items : cus, dn, r, s);
-
-    combine_kernel<uint16_t><<<ceil_div(B * (d / 4), kThreads), kThreads, 0, s>>>(
-        part, pos, r.topk_ids, r.topk_w, B, d, k, static_cast<uint16_t *>(y));
+    if (B <= 16)
+      launch_ffn<1>(grid, p, r, s);
+    else if (B <= 32)
+      launch_ffn<2>(grid, p, r, s);
+    else
+      launch_ffn<4>(grid, p, r, s);
   } else {
     float *h = reinterpret_cast<float *>(ws + plan.h);
     up_f32_kernel<<<ceil_div(P * I, kThreads), kThreads, 0, s>>>(
@@ -716,7 +888,7 @@ hipError_t launch_expert_ffn(const void *x, const void *w_gate, const void *w_up
     down_f32_kernel<<<ceil_div(P * d, kThreads), kThreads, 0, s>>>(
         h, static_cast<const float *>(w_down), d, I, k, r.n_active, r.expert_offsets,
         r.pair_token, r.pair_slot, r.topk_ids, part);
-    combine_kernel<float><<<ceil_div(B * (d / 4), kThreads), kThreads, 0, s>>>(
+    combine_f32_kernel<<<ceil_div(B * (d / 4), kThreads), kThreads, 0, s>>>(
         part, pos, r.topk_ids, r.topk_w, B, d, k, static_cast<float *>(y));
   }
   return hipGetLastError();

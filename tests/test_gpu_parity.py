@@ -52,7 +52,16 @@ def _run_layer(cfg: LayerConfig, inp, dev, B: int, policy: str, k0: int, m: int,
     torch.cuda.synchronize()
     if guard:
         assert lg.intact() and y.intact(), "write past the end of an output buffer"
+    _assert_sync_words_clear(ws)
     return lg.t.cpu().numpy(), routing_numpy(r), y.t
+
+
+def _assert_sync_words_clear(ws):
+    """The FFN's grid-barrier count returns to zero and its error word stays
+    zero (a barrier wait never ran out)."""
+    words = ws[:512].view(torch.int32).cpu().numpy()
+    assert words[0] == 0, f"barrier count left at {words[0]}"
+    assert words[64] == 0, "a grid-barrier wait exceeded its bound"
 
 
 def _oracle(cfg, inp, B, policy, k0, m, tokens=None):
@@ -102,6 +111,30 @@ def test_layer_is_deterministic():
         assert np.array_equal(rg["ids"], outs[0][1]["ids"])
         assert np.array_equal(rg["w"], outs[0][1]["w"])
         assert torch.equal(y, outs[0][2])
+
+
+def test_workspace_reused_across_calls():
+    """One workspace serves many calls in a row (the barrier words carry over)."""
+    cfg = CONFIGS["qwen3_30b_bf16"]
+    inp, dev = _layer_inputs("qwen3_30b_bf16")
+    B = 16
+    x = dev["x"][:B].contiguous()
+    ws = L.alloc_workspace(B, cfg.d, cfg.E, cfg.I, cfg.k, torch.bfloat16)
+    outs = []
+    for pol, p in (("oea", 4), ("topk", 0), ("budget", 32), ("oea", 4), ("oea", 1)):
+        a = policy_args(pol, p)
+        r = L.Routing(B, cfg.E, cfg.k)
+        lg = torch.empty((B, cfg.E), dtype=torch.float32, device="cuda")
+        y = torch.empty((B, cfg.d), dtype=torch.bfloat16, device="cuda")
+        L.moe_layer_decode(x, dev["w_g"], dev["bias"], dev["w_gate"], dev["w_up"], dev["w_down"],
+                           L.make_policy(a["policy"], cfg.k, a["k0"], a["m"]), lg, r, y, ws)
+        torch.cuda.synchronize()
+        _assert_sync_words_clear(ws)
+        outs.append(y.clone())
+    assert torch.equal(outs[0], outs[3])
+    # Fresh workspace, same call: same bits.
+    _, _, y_fresh = _run_layer(cfg, inp, dev, B, "oea", 1, 0)
+    assert torch.equal(outs[4], y_fresh)
 
 
 def test_route_select_ffn_equal_layer():
