@@ -51,7 +51,8 @@ static_assert(kStripCols == 64 && kBK == 128, "tile constants");
 // Routing lists staged in LDS once per workgroup (the loop reads them with
 // the inline-assembly helpers below).
 constexpr int kMetaTok = 0;                            // uint8 token of each pair
-constexpr int kMetaAct = kMetaTok + kMaxPairs;         // int16 active expert list
+constexpr int kMetaRow = kMetaTok + kMaxPairs;         // int16 token slot t*k+j of each pair
+constexpr int kMetaAct = kMetaRow + 2 * kMaxPairs;     // int16 active expert list
 constexpr int kMetaOff = kMetaAct + 2 * kMaxE;         // int16 CSR offsets
 constexpr int kMetaBytes = kMetaOff + 2 * (kMaxE + 1) + 14;
 
@@ -124,8 +125,10 @@ __device__ __forceinline__ float ld_dev(const float *p) {
 __device__ __forceinline__ int32_t ld_dev(const int32_t *p) {
   return __hip_atomic_load(const_cast<int32_t *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ float4 ld_dev4(const float *p) {
-  return make_float4(ld_dev(p), ld_dev(p + 1), ld_dev(p + 2), ld_dev(p + 3));
+// 16 bytes at byte offset `off` of buffer r, device scope.
+__device__ __forceinline__ float4 ld_dev4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  const f32x4_t v = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, int(off), 0, kPolicyDevice));
+  return make_float4(v[0], v[1], v[2], v[3]);
 }
 
 // s_waitcnt vmcnt(N) lgkmcnt(0), then s_barrier. Compiler barriers keep LDS
@@ -261,13 +264,12 @@ __device__ __forceinline__ void grid_barrier(uint32_t *sync) {
 struct Params {
   const uint16_t *x;          // [B, d]
   const uint16_t *W[3];       // G, U: [E, d, I]; D: [E, I, d]
-  int B, d, I, k;
+  int B, d, E, I, k;
   int slices, slice_rows;     // gate/up reduction slices over d
   int P;                      // B * k
   float *gpart;               // [slices][2][P][I] gate/up partial sums by pair
   uint16_t *h;                // [P][I] SiLU(g) * u by pair
-  float *part;                // [P][d] down-projection rows by pair
-  int32_t *pair_of_slot;      // [P] pair index of token slot t*k+j
+  float *part;                // [P][d] down-projection rows by token slot t*k+j
   uint16_t *y;                // [B][d]
   const int32_t *ids;         // [B][k]
   const float *w;             // [B][k]
@@ -512,12 +514,13 @@ __device__ __forceinline__ void compute_stage(uint32_t slot, const uint32_t (&tr
   else mfma_stage<MTX, (MTX >= 4 ? 4 : 1)>(slot, xslot, trc, xrd, acc);
 }
 
-// Stores the accumulators of the pass that just ended, by pair: the gate and
-// up partial sums of slice ks, or two 64-column tiles of the down projection.
+// Stores the accumulators of the pass that just ended: the gate and up partial
+// sums of slice ks by pair, or two 64-column tiles of the down projection by
+// token slot.
 // A pass has at most 16 * MTX tokens.
 template <int MTX>
-__device__ __forceinline__ void epilogue(const Cursor &c, const Params &p, int wave, int lane,
-                                         Acc &acc) {
+__device__ __forceinline__ void epilogue(const Cursor &c, const Params &p, uint32_t meta, int wave,
+                                         int lane, Acc &acc) {
   const int g = lane >> 4, j = lane & 15;
   const int T = min(kMaxTok, c.T - c.pass * kMaxTok);
   const int pbase = c.p0 + c.pass * kMaxTok;
@@ -549,7 +552,7 @@ __device__ __forceinline__ void epilogue(const Cursor &c, const Params &p, int w
 #pragma unroll
       for (int m = 0; m < kDotMaxT; ++m)
         if (m < T) {
-          const size_t row = size_t(pbase + m) * ld;
+          const size_t row = size_t(c.up ? pbase + m : lds_i16(meta + kMetaRow + 2 * (pbase + m))) * ld;
           if (ok0) st_dev(dst0 + row + col0, acc.dot[0][m]);
           if (ok1) st_dev(dst1 + row + col1, acc.dot[1][m]);
         }
@@ -562,31 +565,31 @@ __device__ __forceinline__ void epilogue(const Cursor &c, const Params &p, int w
     for (int i = 0; i < 4; ++i) {
       const int m = 16 * t4 + 4 * g + i;
       if (m < T) {
-        const size_t row = size_t(pbase + m) * ld;
+        const size_t row = size_t(c.up ? pbase + m : lds_i16(meta + kMetaRow + 2 * (pbase + m))) * ld;
         if (ok0) st_dev(dst0 + row + col0, acc.mf[0][t4][i]);
         if (ok1) st_dev(dst1 + row + col1, acc.mf[1][t4][i]);
       }
     }
 }
 
-// h = SiLU(g) * u from the slice partial sums, spread over the whole grid;
-// also the pair index of every token slot, for the combine. All loads of a
-// thread are issued before the first is used.
+// h = SiLU(g) * u from the slice partial sums, spread over the whole grid.
+// All loads of a thread are issued before the first is used.
 __device__ __forceinline__ void h_phase(const Params &p, int total) {
   const int q4 = p.I / 4;
   const int n = total * q4;
+  const uint32_t blk = uint32_t(p.P) * uint32_t(p.I) * 4u;  // bytes of one [P][I] block
   for (int idx = blockIdx.x * kThreads + threadIdx.x; idx < n; idx += gridDim.x * kThreads) {
     const int pr = idx / q4;
     const int c = (idx - pr * q4) * 4;
+    const uint32_t off = (uint32_t(pr) * uint32_t(p.I) + uint32_t(c)) * 4u;
     float4 gv[kUpMaxSlices], uv[kUpMaxSlices];
 #pragma unroll
     for (int s = 0; s < kUpMaxSlices; ++s) {
       if (s < p.slices) {
-        gv[s] = ld_dev4(p.gpart + ((size_t(s) * 2 + 0) * p.P + pr) * p.I + c);
-        uv[s] = ld_dev4(p.gpart + ((size_t(s) * 2 + 1) * p.P + pr) * p.I + c);
+        gv[s] = ld_dev4(make_rsrc(p.gpart + size_t(s * 2 + 0) * p.P * p.I, blk), off);
+        uv[s] = ld_dev4(make_rsrc(p.gpart + size_t(s * 2 + 1) * p.P * p.I, blk), off);
       }
     }
-    if (c == 0) st_dev(p.pair_of_slot + p.pair_token[pr] * p.k + p.pair_slot[pr], pr);
     float4 g = make_float4(0, 0, 0, 0), u = make_float4(0, 0, 0, 0);
 #pragma unroll
     for (int s = 0; s < kUpMaxSlices; ++s) {
@@ -603,34 +606,32 @@ __device__ __forceinline__ void h_phase(const Params &p, int total) {
   }
 }
 
-// y[t] = sum over slots j in order of w[t,j] * part[pair of (t,j)] (empty
-// slots skipped), spread over the whole grid. A thread first loads its
-// token's slot lists, then every part row it needs, then sums.
+// y[t] = sum over slots j in order of w[t,j] * part[t*k+j] (empty slots
+// skipped), spread over the whole grid; every load of a thread is issued
+// before the first is used.
 __device__ __forceinline__ void combine_phase(const Params &p) {
   const int q4 = p.d / 4;
   const int n = p.B * q4;
+  const __amdgpu_buffer_rsrc_t rp = make_rsrc(p.part, uint32_t(p.P) * uint32_t(p.d) * 4u);
   for (int idx = blockIdx.x * kThreads + threadIdx.x; idx < n; idx += gridDim.x * kThreads) {
     const int t = idx / q4;
     const int c = (idx - t * q4) * 4;
-    int pos[kMaxK];
+    int id[kMaxK];
     float w[kMaxK];
-#pragma unroll
-    for (int j = 0; j < kMaxK; ++j) {
-      pos[j] = -1;
-      w[j] = 0.f;
-      if (j < p.k && p.ids[t * p.k + j] >= 0) {
-        pos[j] = ld_dev(p.pair_of_slot + t * p.k + j);
-        w[j] = p.w[t * p.k + j];
-      }
-    }
     float4 v[kMaxK];
 #pragma unroll
-    for (int j = 0; j < kMaxK; ++j)
-      if (pos[j] >= 0) v[j] = ld_dev4(p.part + size_t(pos[j]) * p.d + c);
+    for (int j = 0; j < kMaxK; ++j) {
+      if (j < p.k) {
+        const int slot = t * p.k + j;
+        id[j] = p.ids[slot];
+        w[j] = p.w[slot];
+        v[j] = ld_dev4(rp, (uint32_t(slot) * uint32_t(p.d) + uint32_t(c)) * 4u);
+      }
+    }
     float4 acc = make_float4(0, 0, 0, 0);
 #pragma unroll
     for (int j = 0; j < kMaxK; ++j) {
-      if (pos[j] >= 0) {
+      if (j < p.k && id[j] >= 0) {
         acc.x = fmaf(w[j], v[j].x, acc.x);
         acc.y = fmaf(w[j], v[j].y, acc.y);
         acc.z = fmaf(w[j], v[j].z, acc.z);
@@ -667,14 +668,20 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_kernel(Params p,
   unsigned char *stages = lds;
   unsigned char *meta = lds + kS * S::kSlot;
 
+  // Routing lists into LDS, in one round of independent loads (entries past
+  // the active ones are never read).
   const int nact = n_active[0];
-  const int total = offsets[nact];
-  for (int i = threadIdx.x; i <= nact; i += kThreads) {
+  for (int i = threadIdx.x; i <= p.E; i += kThreads) {
     reinterpret_cast<int16_t *>(meta + kMetaOff)[i] = int16_t(offsets[i]);
-    if (i < nact) reinterpret_cast<int16_t *>(meta + kMetaAct)[i] = int16_t(active[i]);
+    if (i < p.E) reinterpret_cast<int16_t *>(meta + kMetaAct)[i] = int16_t(active[i]);
   }
-  for (int i = threadIdx.x; i < total; i += kThreads) meta[kMetaTok + i] = uint8_t(p.pair_token[i]);
+  for (int i = threadIdx.x; i < p.P; i += kThreads) {
+    const int t = p.pair_token[i];
+    meta[kMetaTok + i] = uint8_t(t);
+    reinterpret_cast<int16_t *>(meta + kMetaRow)[i] = int16_t(t * p.k + p.pair_slot[i]);
+  }
   __syncthreads();
+  const int total = reinterpret_cast<const int16_t *>(meta + kMetaOff)[nact];
 
   const Stream<MTX> st(p, lds_addr(meta));
   Cursor cons;
@@ -731,7 +738,7 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_kernel(Params p,
     }
     compute_stage<MTX>(base + uint32_t((s % kS) * S::kSlot), st.trc, st.xrd, st.dotrd, st.tp(cons), acc);
     if (cons.kst == cons.nst - 1) {
-      epilogue<MTX>(cons, p, st.wave, st.lane, acc);
+      epilogue<MTX>(cons, p, st.meta, st.wave, st.lane, acc);
       clear(acc);
     }
     st.advance(cons);
@@ -851,6 +858,7 @@ hipError_t launch_expert_ffn(const void *x, const void *w_gate, const void *w_up
     p.W[2] = static_cast<const uint16_t *>(w_down);
     p.B = B;
     p.d = d;
+    p.E = E;
     p.I = I;
     p.k = k;
     p.slices = plan.up_slices;
@@ -859,7 +867,6 @@ hipError_t launch_expert_ffn(const void *x, const void *w_gate, const void *w_up
     p.gpart = reinterpret_cast<float *>(ws + plan.up_part);
     p.h = reinterpret_cast<uint16_t *>(ws + plan.h);
     p.part = part;
-    p.pair_of_slot = pos;
     p.y = static_cast<uint16_t *>(y);
     p.ids = r.topk_ids;
     p.w = r.topk_w;

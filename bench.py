@@ -4,10 +4,11 @@ MI355X: layer latency, active-expert count and expert-weight HBM bandwidth.
 
 One step = one moe_layer_decode call (router, selection, gate weights,
 compaction, grouped SwiGLU FFN) over one batch of seeded synthetic tokens.
-Steps are replayed from HIP graphs and rotate over R bit-identical copies of
-the weights at different addresses, so the 256 MB Infinity Cache cannot serve
-the active experts from one step to the next. Inputs are resident in HBM
-before the timed region starts.
+Steps are replayed from HIP graphs, each chaining R steps over R
+bit-identical copies of the weights at different addresses, so the 256 MB
+Infinity Cache cannot serve the active experts from one step to the next.
+Inputs are resident in HBM before the timed region starts. Percentiles are
+over graph replays (per-step averages within one replay).
 
 Prints one JSON line (rank 0, N = 1). `value` is the active-expert weight
 bytes of one step divided by the measured step time (GB/s).
@@ -96,41 +97,48 @@ class Case:
         self.L.moe_expert_ffn(self.x, d["w_gate"], d["w_up"], d["w_down"], self.routing, self.y, self.ws)
 
 
-def _capture(fn, n):
+def _capture_chain(fn, first, count):
+    """One HIP graph of `count` consecutive calls fn(first), fn(first+1), ...
+    (each on its own weight replica)."""
     import torch
-    graphs = []
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for r in range(first, first + count):
+            fn(r)
+    return g
+
+
+def _time_steps(fn, R, steps, warmup):
+    """Times exactly `steps` calls of fn, replayed from graphs that chain R
+    calls (one per replica) plus one tail graph, with events recorded on the
+    replay stream between graph launches. Returns per-call times (ms) of each
+    replay and the total over the timed region."""
+    import torch
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(s):
-        for r in range(n):  # warm the code paths outside capture
+        for r in range(R):  # warm the code paths outside capture
             fn(r)
     torch.cuda.current_stream().wait_stream(s)
     torch.cuda.synchronize()
-    for r in range(n):
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            fn(r)
-        graphs.append(g)
+    full = _capture_chain(fn, 0, R)
+    n_full, tail_n = divmod(steps, R)
+    tail = _capture_chain(fn, 0, tail_n) if tail_n else None
     torch.cuda.synchronize()
-    return graphs
-
-
-def _time_graphs(graphs, steps, warmup):
-    """Per-step times (ms) from events recorded between graph replays on the
-    replay stream, plus the total over the timed region."""
-    import torch
-    n = len(graphs)
-    for i in range(warmup):
-        graphs[i % n].replay()
+    for _ in range(max(1, warmup // R)):
+        full.replay()
     torch.cuda.synchronize()
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    plan = [(full, R)] * n_full + ([(tail, tail_n)] if tail else [])
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(plan) + 1)]
     ev[0].record()
-    for i in range(steps):
-        graphs[i % n].replay()
+    for i, (g, _) in enumerate(plan):
+        g.replay()
         ev[i + 1].record()
     torch.cuda.synchronize()
-    per = [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]
-    return per, ev[0].elapsed_time(ev[-1])
+    per = [ev[i].elapsed_time(ev[i + 1]) / n for i, (_, n) in enumerate(plan)]
+    total = ev[0].elapsed_time(ev[-1])
+    del full, tail
+    return per, total
 
 
 def _cpu_baseline(cfg, inp, B, policy, k0, m, active_bytes, seconds):
@@ -160,15 +168,12 @@ def _run_case(cfg, B, policy, k0, m, inp, dev, args, with_cpu):
 
     c = Case(cfg, B, policy, k0, m, inp, dev, args.rotate_bytes)
     R = len(c.replicas)
-    g_layer = _capture(c.layer, R)
-    per, total = _time_graphs(g_layer, args.steps, args.warmup)
+    per, total = _time_steps(c.layer, R, args.steps, args.warmup)
     med, p10, p90 = _percentiles(per)
     ms_per_step = total / args.steps
-    g_ffn = _capture(c.ffn, R)
-    per_f, total_f = _time_graphs(g_ffn, args.steps, args.warmup)
-    ffn_med, _, _ = _percentiles(per_f)
+    # The expert FFN alone (one kernel for bf16): its average launch time.
+    _, total_f = _time_steps(c.ffn, R, args.steps, args.warmup)
     ffn_ms = total_f / args.steps
-    del g_layer, g_ffn
     value = c.active_bytes / (ms_per_step * 1e-3) / 1e9
     ffn_gbps = c.active_bytes / (ffn_ms * 1e-3) / 1e9
     pol = policy + (f"(k0={k0})" if policy == "oea" else f"(m={m})" if policy == "budget" else "")
@@ -197,7 +202,7 @@ def _run_case(cfg, B, policy, k0, m, inp, dev, args, with_cpu):
         "expert_ffn_us": round(ffn_ms * 1e3, 2),
         "roofline": {"bound": "hbm", "achieved": round(ffn_gbps, 1), "peak": PEAK_HBM_GBPS,
                      "unit": "GB/s", "frac": round(ffn_gbps / PEAK_HBM_GBPS, 4), "traffic": None,
-                     "kernel": "expert FFN (moe_expert_ffn: gate/up, SwiGLU, down, combine)",
+                     "kernel": "ffn_kernel (moe_expert_ffn: gate/up, SwiGLU, down and combine, one launch)",
                      "bytes_per_launch": c.active_bytes},
     }
     if with_cpu:
