@@ -57,9 +57,10 @@ moe_status_t check_workspace(const void *ws, size_t have, size_t need) {
 }
 
 // moe_route writes its partial sums where the full plan puts them, after the
-// grid-barrier words, so that a workspace can serve every entry point.
+// expert FFN's synchronisation words, so that a workspace can serve every
+// entry point.
 size_t route_bytes(int B, int d, int E) {
-  return kSyncBytes + align256(size_t(ceil_div(d, kRouterRows)) * B * E * sizeof(float));
+  return router_offset(B, d) + align256(size_t(ceil_div(d, kRouterRows)) * B * E * sizeof(float));
 }
 
 #define MOE_TRY(expr)                     \
@@ -90,7 +91,7 @@ moe_status_t moe_route(const void *x, const void *w_g, const float *bias, moe_dt
   if (bias && !aligned(bias, 4)) return MOE_ERR_INVALID_ARG;
   MOE_TRY(check_workspace(workspace, workspace_bytes, route_bytes(B, d, E)));
   hipStream_t s = static_cast<hipStream_t>(stream);
-  float *part = reinterpret_cast<float *>(static_cast<char *>(workspace) + kSyncBytes);
+  float *part = reinterpret_cast<float *>(static_cast<char *>(workspace) + router_offset(B, d));
   const int slices = ceil_div(d, kRouterRows);
   MOE_TRY(hip_status(launch_router(x, w_g, dt, B, d, E, part, slices, s)));
   return hip_status(launch_router_reduce(part, bias, slices, B, E, logits, s));

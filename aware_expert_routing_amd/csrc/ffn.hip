@@ -5,25 +5,28 @@
 // "Opportunistic Expert Activation", abstract: MoE latency is governed by the
 // number of activated experts).
 //
-// bf16 path. Both products (gate/up: A = x, W = G and U; down: A = h, W = D)
-// run through one persistent streaming kernel:
-//   * a work item is one active expert x one 64-column strip of the output x
-//     one slice of the reduction; a workgroup takes items b, b+G, b+2G, ...;
-//   * the workgroup's items form one flat sequence of 64-row stages; stages
-//     are copied HBM -> LDS by buffer_load ... lds (no registers involved) into
-//     a ring of slots, several stages ahead of the one being used, so the copy
-//     of the next item's weights overlaps the end of the current one;
-//   * each wave counts the copies it has issued and waits with s_waitcnt
-//     vmcnt(n) for exactly the stage it needs, then one s_barrier;
-//   * weight rows are stored with their 16-byte chunks XOR-swizzled so that
+// bf16 path: one persistent kernel, one workgroup per CU.
+//   * Work items: gate/up items (active expert x 64-column strip of I x slice
+//     of d) come first, then down items (active expert x 128-column strip of
+//     d x all of I); workgroup b takes items b, b+G, b+2G, ...
+//   * Every item is a sequence of stages of kBK reduction rows; a stage holds
+//     two weight tiles (G and U, or two adjacent 64-column tiles of D) and the
+//     A tile of the same rows (x rows gathered by token, or h rows by pair).
+//     Stages are copied HBM -> LDS with buffer_load ... lds (no registers
+//     involved) into a ring of slots, several stages ahead of the one in use,
+//     across item and phase boundaries.
+//   * Each wave counts the copies it has issued and waits with s_waitcnt
+//     vmcnt(n) for exactly the stage it needs, then one s_barrier.
+//   * Weight rows are stored with their 16-byte chunks XOR-swizzled so that
 //     the transposing LDS reads (ds_read_b64_tr_b16) that build MFMA B
-//     fragments along the reduction dimension are bank-conflict free;
-//   * an expert's tokens form the A operand (16 rows per MFMA tile,
-//     v_mfma_f32_16x16x32_bf16). Experts with at most kDotMaxT tokens use
-//     wave-level v_dot2_f32_bf16 dot products on the same fragments instead.
-// Gate/up partial sums per slice and down-projection outputs per (token, slot)
-// go to the workspace; small kernels finish the SwiGLU (h) and the weighted,
-// fixed-order combine over slots (no float atomics).
+//     fragments along the reduction dimension are bank-conflict free.
+//   * An expert's tokens form the A operand: 16-row tiles of
+//     v_mfma_f32_16x16x32_bf16, up to 64 tokens per pass.
+//   * Gate/up slice partial sums go to the workspace; after a grid barrier
+//     the grid forms h = SiLU(g) * u; after a second one the down items run.
+//   * A down pass counts its tokens on per-(token, strip) counters; the
+//     workgroup that completes a token's count forms y for that strip, adding
+//     the slots in order (no float atomics: results are reproducible).
 // float32 path (small layers): direct per-output dot products.
 #include "moe_internal.h"
 
@@ -42,7 +45,6 @@ constexpr int kKSteps = kBK / 32;               // MFMA k-steps per stage
 constexpr int kRowBytes = kStripCols * 2;       // one strip row of bf16
 constexpr int kWTile = kBK * kRowBytes;         // bytes of one weight matrix per stage
 constexpr int kMaxTok = 64;                     // tokens per pass (4 MFMA row tiles)
-constexpr int kDotMaxT = 4;                     // experts with <= this many tokens use dot2
 constexpr int kMaxPairs = kMaxB * kMaxK;
 constexpr int kRsrcWord3 = 0x00020000;          // raw buffer, gfx9 data format
 constexpr int kLdsBytes = 160 * 1024;
@@ -54,7 +56,9 @@ constexpr int kMetaTok = 0;                            // uint8 token of each pa
 constexpr int kMetaRow = kMetaTok + kMaxPairs;         // int16 token slot t*k+j of each pair
 constexpr int kMetaAct = kMetaRow + 2 * kMaxPairs;     // int16 active expert list
 constexpr int kMetaOff = kMetaAct + 2 * kMaxE;         // int16 CSR offsets
-constexpr int kMetaBytes = kMetaOff + 2 * (kMaxE + 1) + 14;
+constexpr int kMetaLast = kMetaOff + 2 * (kMaxE + 1);  // int32 tokens whose strip this pass completes
+constexpr int kMetaNLast = kMetaLast + 4 * kMaxTok;    // int32 their number
+constexpr int kMetaBytes = kMetaNLast + 16;
 
 // LDS plan of one instantiation. A stage slot holds NMAT weight tiles
 // [kBK rows][64 columns] and the A tile, stored per k-step as
@@ -276,6 +280,8 @@ struct Params {
   const int32_t *pair_token;  // [P]
   const int32_t *pair_slot;   // [P]
   uint32_t *sync;             // grid-barrier words
+  uint32_t *tok_cnt;          // [B][n_dstrips] down passes counted per (token, strip)
+  int n_dstrips;              // 128-column strips of d
 };
 
 // A position in a workgroup's stage sequence. The workgroup's items are
@@ -300,7 +306,6 @@ struct Stream {
   uint32_t wv_dn[4];        // the same for D (row stride d)
   uint32_t trc[2];          // transposing-read offsets within a weight tile
   uint32_t xrd;             // A-fragment read offset within a k-step sub-tile
-  uint32_t dotrd;           // token-row read offset for the dot2 path
 
   __device__ __forceinline__ Stream(const Params &pp, uint32_t meta_addr) : p(pp), meta(meta_addr) {
     wave = wave_id();
@@ -321,7 +326,6 @@ struct Stream {
       trc[h] = uint32_t(R * kRowBytes + ((c ^ swz_w(R)) << 4) + ((j & 1) << 3));
     }
     xrd = uint32_t(j * 64 + ((g ^ swz_x(j)) << 4));
-    dotrd = uint32_t(g << 4);
   }
 
   __device__ __forceinline__ void decode(Cursor &c) const {
@@ -420,8 +424,7 @@ struct Stream {
 };
 
 struct Acc {
-  f32x4_t mf[2][4];        // MFMA: rows 4*(lane/16)+i of tile mt, column 16*wave + lane%16
-  float dot[2][kDotMaxT];  // dot2: token m over this lane's k-groups
+  f32x4_t mf[2][4];  // rows 4*(lane/16)+i of tile mt, column 16*wave + lane%16
 };
 
 __device__ __forceinline__ void clear(Acc &acc) {
@@ -429,8 +432,6 @@ __device__ __forceinline__ void clear(Acc &acc) {
   for (int mat = 0; mat < 2; ++mat) {
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) acc.mf[mat][mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int m = 0; m < kDotMaxT; ++m) acc.dot[mat][m] = 0.f;
   }
 }
 
@@ -465,48 +466,9 @@ __device__ __forceinline__ void mfma_stage(uint32_t slot, uint32_t xslot, const 
 }
 
 template <int MTX>
-__device__ __forceinline__ void dot_stage(uint32_t slot, uint32_t xslot, const uint32_t (&trc)[2],
-                                          uint32_t dotrd, int T, Acc &acc) {
-#pragma unroll
-  for (int ks = 0; ks < kKSteps; ++ks) {
-    bf16x8_t b[2];
-    b_frags(slot, trc, ks, b);
-    // Rows 0..3 of the k-step's A sub-tile: token m's 8 values of this lane's
-    // k-group (rows below 4 are not swizzled).
-    const uint32_t xb = xslot + uint32_t(ks * Shape<2, MTX>::kXSub) + dotrd;
-    const uint32_t aa[4] = {xb, xb + 64, xb + 128, xb + 192};
-    bf16x8_t a[4];
-    lds_b128<4>(aa, a);
-#pragma unroll
-    for (int m = 0; m < kDotMaxT; ++m) {
-      if (m < T) {
-#pragma unroll
-        for (int mat = 0; mat < 2; ++mat) {
-          float s = acc.dot[mat][m];
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            bf16x2_t wv, xv;
-            wv[0] = b[mat][2 * q];
-            wv[1] = b[mat][2 * q + 1];
-            xv[0] = a[m][2 * q];
-            xv[1] = a[m][2 * q + 1];
-            s = __builtin_amdgcn_fdot2_f32_bf16(wv, xv, s, false);
-          }
-          acc.dot[mat][m] = s;
-        }
-      }
-    }
-  }
-}
-
-template <int MTX>
 __device__ __forceinline__ void compute_stage(uint32_t slot, const uint32_t (&trc)[2], uint32_t xrd,
-                                              uint32_t dotrd, int T, Acc &acc) {
+                                              int T, Acc &acc) {
   const uint32_t xslot = slot + 2 * kWTile;
-  if (T <= kDotMaxT) {
-    dot_stage<MTX>(slot, xslot, trc, dotrd, T, acc);
-    return;
-  }
   const int na = (T + 15) >> 4;
   if (MTX == 1 || na == 1) mfma_stage<MTX, 1>(slot, xslot, trc, xrd, acc);
   else if (MTX == 2 || na == 2) mfma_stage<MTX, (MTX >= 2 ? 2 : 1)>(slot, xslot, trc, xrd, acc);
@@ -538,27 +500,6 @@ __device__ __forceinline__ void epilogue(const Cursor &c, const Params &p, uint3
     dst0 = dst1 = p.part;
   }
   const bool ok0 = col0 < ld, ok1 = col1 < ld;
-  if (T <= kDotMaxT) {
-#pragma unroll
-    for (int mat = 0; mat < 2; ++mat)
-#pragma unroll
-      for (int m = 0; m < kDotMaxT; ++m) {
-        float v = acc.dot[mat][m];
-        v += __shfl_xor(v, 16);
-        v += __shfl_xor(v, 32);
-        acc.dot[mat][m] = v;
-      }
-    if (g == 0) {
-#pragma unroll
-      for (int m = 0; m < kDotMaxT; ++m)
-        if (m < T) {
-          const size_t row = size_t(c.up ? pbase + m : lds_i16(meta + kMetaRow + 2 * (pbase + m))) * ld;
-          if (ok0) st_dev(dst0 + row + col0, acc.dot[0][m]);
-          if (ok1) st_dev(dst1 + row + col1, acc.dot[1][m]);
-        }
-    }
-    return;
-  }
 #pragma unroll
   for (int t4 = 0; t4 < MTX; ++t4)
 #pragma unroll
@@ -606,53 +547,86 @@ __device__ __forceinline__ void h_phase(const Params &p, int total) {
   }
 }
 
-// y[t] = sum over slots j in order of w[t,j] * part[t*k+j] (empty slots
-// skipped), spread over the whole grid; every load of a thread is issued
-// before the first is used.
-__device__ __forceinline__ void combine_phase(const Params &p) {
-  const int q4 = p.d / 4;
-  const int n = p.B * q4;
-  const __amdgpu_buffer_rsrc_t rp = make_rsrc(p.part, uint32_t(p.P) * uint32_t(p.d) * 4u);
-  for (int idx = blockIdx.x * kThreads + threadIdx.x; idx < n; idx += gridDim.x * kThreads) {
-    const int t = idx / q4;
-    const int c = (idx - t * q4) * 4;
-    int id[kMaxK];
-    float w[kMaxK];
-    float4 v[kMaxK];
-#pragma unroll
-    for (int j = 0; j < kMaxK; ++j) {
-      if (j < p.k) {
-        const int slot = t * p.k + j;
-        id[j] = p.ids[slot];
-        w[j] = p.w[slot];
-        v[j] = ld_dev4(rp, (uint32_t(slot) * uint32_t(p.d) + uint32_t(c)) * 4u);
-      }
+// End of a down pass (its rows stored by every wave). Each token of the pass
+// is counted on its (token, strip) counter; the workgroup that brings the
+// count to the token's number of filled slots forms y[t] over the strip,
+// adding w[t,j] * part[t*k+j] in slot order (empty slots skipped), and resets
+// the counter. A count is taken only after this workgroup's stores have
+// completed, so the last one finds every row of the token in place.
+__device__ __forceinline__ void finish_down(const Cursor &c, const Params &p, unsigned char *meta,
+                                            int wave, int lane) {
+  const int T = min(kMaxTok, c.T - c.pass * kMaxTok);
+  const int pbase = c.p0 + c.pass * kMaxTok;
+  int32_t *last = reinterpret_cast<int32_t *>(meta + kMetaLast);
+  int32_t *n_last = reinterpret_cast<int32_t *>(meta + kMetaNLast);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  if (wave == 0) {
+    bool mine = false;
+    int t = 0;
+    if (lane < T) {
+      t = meta[kMetaTok + pbase + lane];
+      int filled = 0;
+      for (int j = 0; j < p.k; ++j) filled += p.ids[t * p.k + j] >= 0;
+      const uint32_t before = __hip_atomic_fetch_add(p.tok_cnt + t * p.n_dstrips + c.strip, 1u,
+                                                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      mine = before == uint32_t(filled - 1);
     }
-    float4 acc = make_float4(0, 0, 0, 0);
-#pragma unroll
-    for (int j = 0; j < kMaxK; ++j) {
-      if (j < p.k && id[j] >= 0) {
-        acc.x = fmaf(w[j], v[j].x, acc.x);
-        acc.y = fmaf(w[j], v[j].y, acc.y);
-        acc.z = fmaf(w[j], v[j].z, acc.z);
-        acc.w = fmaf(w[j], v[j].w, acc.w);
-      }
-    }
-    ushort4 o;
-    o.x = f32_to_bf16(acc.x);
-    o.y = f32_to_bf16(acc.y);
-    o.z = f32_to_bf16(acc.z);
-    o.w = f32_to_bf16(acc.w);
-    *reinterpret_cast<ushort4 *>(p.y + size_t(t) * p.d + c) = o;
+    const unsigned long long b = __ballot(mine);
+    if (mine) last[__builtin_amdgcn_mbcnt_hi(uint32_t(b >> 32), __builtin_amdgcn_mbcnt_lo(uint32_t(b), 0))] = t;
+    if (lane == 0) *n_last = __popcll(b);
   }
+  __syncthreads();
+  const int n = *n_last;
+  const __amdgpu_buffer_rsrc_t rp = make_rsrc(p.part, uint32_t(p.P) * uint32_t(p.d) * 4u);
+  constexpr int kGroups = 2 * kStripCols / 4;  // 4-column groups of a strip
+  for (int i = threadIdx.x; i < n * kGroups; i += kThreads) {
+    const int t = last[i / kGroups];
+    const int col = c.strip * 2 * kStripCols + (i % kGroups) * 4;
+    if (col < p.d) {
+      int id[kMaxK];
+      float w[kMaxK];
+      float4 v[kMaxK];
+#pragma unroll
+      for (int j = 0; j < kMaxK; ++j) {
+        if (j < p.k) {
+          const int slot = t * p.k + j;
+          id[j] = p.ids[slot];
+          w[j] = p.w[slot];
+          v[j] = ld_dev4(rp, (uint32_t(slot) * uint32_t(p.d) + uint32_t(col)) * 4u);
+        }
+      }
+      float4 acc = make_float4(0, 0, 0, 0);
+#pragma unroll
+      for (int j = 0; j < kMaxK; ++j) {
+        if (j < p.k && id[j] >= 0) {
+          acc.x = fmaf(w[j], v[j].x, acc.x);
+          acc.y = fmaf(w[j], v[j].y, acc.y);
+          acc.z = fmaf(w[j], v[j].z, acc.z);
+          acc.w = fmaf(w[j], v[j].w, acc.w);
+        }
+      }
+      ushort4 o;
+      o.x = f32_to_bf16(acc.x);
+      o.y = f32_to_bf16(acc.y);
+      o.z = f32_to_bf16(acc.z);
+      o.w = f32_to_bf16(acc.w);
+      *reinterpret_cast<ushort4 *>(p.y + size_t(t) * p.d + col) = o;
+    }
+    if (i % kGroups == 0)
+      __hip_atomic_store(p.tok_cnt + t * p.n_dstrips + c.strip, 0u, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __syncthreads();
 }
 
 // The whole bf16 expert FFN in one persistent kernel (one workgroup per CU,
 // all resident together):
 //   1. gate/up items stream G and U and store slice partial sums;
 //   2. grid barrier; h = SiLU(g) * u over the grid; grid barrier;
-//   3. down items stream D with h as the A operand and store rows by pair;
-//   4. grid barrier; weighted combine over the grid.
+//   3. down items stream D with h as the A operand and store rows by token
+//      slot; each token's strip of y is formed by the workgroup that
+//      completes it (finish_down).
 // The ring keeps copying across phases: the first down stages' weights are in
 // flight while the workgroup waits at the barriers; their A tiles are copied
 // once h is complete.
@@ -736,20 +710,19 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_kernel(Params p,
       ++issued;
       st.advance(prod);
     }
-    compute_stage<MTX>(base + uint32_t((s % kS) * S::kSlot), st.trc, st.xrd, st.dotrd, st.tp(cons), acc);
+    compute_stage<MTX>(base + uint32_t((s % kS) * S::kSlot), st.trc, st.xrd, st.tp(cons), acc);
     if (cons.kst == cons.nst - 1) {
       epilogue<MTX>(cons, p, st.meta, st.wave, st.lane, acc);
       clear(acc);
+      if (!cons.up) finish_down(cons, p, meta, st.wave, st.lane);
     }
     st.advance(cons);
   }
-  if (!h_ready) {
+  if (!h_ready) {  // no down items here: still meet the grid twice
     grid_barrier(p.sync);
     h_phase(p, total);
     grid_barrier(p.sync);
   }
-  grid_barrier(p.sync);
-  combine_phase(p);
 }
 
 // ------------------------------------------------------------- combine (f32)
@@ -873,6 +846,8 @@ hipError_t launch_expert_ffn(const void *x, const void *w_gate, const void *w_up
     p.pair_token = r.pair_token;
     p.pair_slot = r.pair_slot;
     p.sync = reinterpret_cast<uint32_t *>(ws + plan.sync);
+    p.tok_cnt = reinterpret_cast<uint32_t *>(ws + plan.tok_cnt);
+    p.n_dstrips = ceil_div(d, 2 * kStripCols);
     // One workgroup per CU at most, so that the whole grid is resident and
     // the grid barriers cannot wait on a workgroup that has not started.
     const int items = max_active * (ceil_div(I, kStripCols) * plan.up_slices + ceil_div(d, 2 * kStripCols));

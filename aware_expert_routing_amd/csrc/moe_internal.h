@@ -31,6 +31,7 @@ inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
 // Workspace carve-up. Every segment starts on a 256-byte boundary.
 struct Workspace {
   size_t sync;         // uint32 grid-barrier words of the expert FFN (kSyncBytes)
+  size_t tok_cnt;      // uint32 [B][ceil(d/128)] per-(token, strip) counters of the expert FFN
   size_t router_part;  // float [router_slices][B][E]
   size_t up_part;      // float [up_slices][2][B*k][I]   (gate, up partial sums)
   size_t h;            // bf16 or float [B*k][I]
@@ -45,9 +46,16 @@ struct Workspace {
 inline size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 
 // Bytes at the start of the workspace that hold the expert FFN's grid-barrier
-// words. They must be zero before the workspace's first use; every call
-// leaves them ready for the next one. No other step writes them.
+// words; its per-token counters follow. Both must be zero before the
+// workspace's first use; every call leaves them ready for the next one. No
+// other step writes them.
 constexpr size_t kSyncBytes = 512;
+
+// Offset of the router's partial sums: after the expert FFN's synchronisation
+// words (barrier words, then per-token counters), which depend on B and d only.
+inline size_t router_offset(int B, int d) {
+  return kSyncBytes + align256(size_t(B) * ceil_div(d, 2 * kStripCols) * sizeof(uint32_t));
+}
 
 inline Workspace plan_workspace(int B, int d, int E, int I, int k, moe_dtype_t dt) {
   Workspace w{};
@@ -62,7 +70,8 @@ inline Workspace plan_workspace(int B, int d, int E, int I, int k, moe_dtype_t d
   const size_t esz = (dt == MOE_BF16) ? 2 : 4;
   size_t off = 0;
   w.sync = off;
-  off += kSyncBytes;
+  w.tok_cnt = off + kSyncBytes;
+  off = router_offset(B, d);
   w.router_part = off;
   off = align256(off + size_t(w.router_slices) * B * E * sizeof(float));
   w.up_part = off;

@@ -108,8 +108,9 @@ typedef struct {
  *
  * The workspace must be zero-filled once, before its first use (e.g.
  * hipMemset after allocation); afterwards the caller must not write it. Its
- * first 512 bytes hold the grid-barrier words of the bf16 expert FFN, which
- * every call leaves ready for the next one. The same workspace may serve
+ * first bytes hold the synchronisation words of the bf16 expert FFN (grid
+ * barrier, per-token counters), which every call leaves ready for the next
+ * one. The same workspace may serve
  * consecutive calls on one stream; calls that may overlap need separate
  * workspaces. The bf16 expert FFN runs one workgroup per compute unit and
  * needs all of them resident together: do not run it next to another kernel
@@ -119,8 +120,8 @@ typedef struct {
 size_t moe_workspace_bytes(int B, int d, int E, int I, int k, moe_dtype_t dt);
 
 /* Step 1 only: logits[B,E] (float32) = x W_g + bias. bias may be NULL (zero).
- * Uses the workspace (after its first 512 bytes) for per-slice partial sums;
- * it needs at least moe_workspace_bytes(B, d, E, 8, 1, dt) bytes. */
+ * Uses the workspace (after the synchronisation words) for per-slice partial
+ * sums; it needs at least moe_workspace_bytes(B, d, E, 8, 1, dt) bytes. */
 moe_status_t moe_route(const void *x, const void *w_g, const float *bias, moe_dtype_t dt,
                        int B, int d, int E, float *logits, void *workspace,
                        size_t workspace_bytes, void *stream);
