@@ -28,6 +28,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBPS = 8000.0
+KERNEL_SOURCES = ("aware_expert_routing_amd/csrc/ffn.hip", "aware_expert_routing_amd/csrc/moe_internal.h")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "ffn_kernel_qwen3_30b_B16_oea4_traffic.json")
 METRIC = "MoE-layer decode µs + expert-weight HBM GB/s (% of peak), B=16, E=128 k=8"
 
 
@@ -47,6 +49,10 @@ def _parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--sweep", default=None,
                     help="run every configured (config, B, policy) case; one JSON line each to this file")
+    ap.add_argument("--ffn-only", type=int, default=0, metavar="N",
+                    help="run N eager moe_expert_ffn calls on rotating replicas and exit (for counter runs)")
+    ap.add_argument("--copy-calibration", type=float, default=0.0, metavar="MB",
+                    help="run a plain device copy of MB megabytes 10 times and exit (counter scale)")
     return ap.parse_args()
 
 
@@ -141,6 +147,30 @@ def _time_steps(fn, R, steps, warmup):
     return per, total
 
 
+def _kernel_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def _traffic(workload):
+    """HBM bytes per launch of the FFN kernel from the committed counter
+    summary (FETCH_SIZE + WRITE_SIZE, each scaled by a plain copy of known
+    size), or None when there is none for this workload or the kernel
+    sources changed since the counters were taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("source_sha256") != _kernel_source_hash() or t.get("workload") != workload:
+        return None
+    return int(t["fetch_bytes"] + t["write_bytes"])
+
+
 def _cpu_baseline(cfg, inp, B, policy, k0, m, active_bytes, seconds):
     from threadpoolctl import threadpool_info
     from oracle import moe_oracle as orc
@@ -177,6 +207,8 @@ def _run_case(cfg, B, policy, k0, m, inp, dev, args, with_cpu):
     value = c.active_bytes / (ms_per_step * 1e-3) / 1e9
     ffn_gbps = c.active_bytes / (ffn_ms * 1e-3) / 1e9
     pol = policy + (f"(k0={k0})" if policy == "oea" else f"(m={m})" if policy == "budget" else "")
+    out_workload = (f"{cfg.name} decode MoE layer, B={B}, d={cfg.d}, E={cfg.E}, k={cfg.k}, "
+                    f"I={cfg.I}, policy {pol}")
     out = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -190,8 +222,7 @@ def _run_case(cfg, B, policy, k0, m, inp, dev, args, with_cpu):
         "vs_baseline": None,
         "dtype": cfg.dtype,
         "data": "synthetic (seeded; shapes and distributions of the named layer)",
-        "config": {"workload": f"{cfg.name} decode MoE layer, B={B}, d={cfg.d}, E={cfg.E}, k={cfg.k}, "
-                               f"I={cfg.I}, policy {pol}",
+        "config": {"workload": out_workload,
                    "batch": B, "policy": pol, "replicas": R},
         "layer_us": {"median": round(med * 1e3, 2), "p10": round(p10 * 1e3, 2),
                      "p90": round(p90 * 1e3, 2), "mean": round(ms_per_step * 1e3, 2)},
@@ -201,7 +232,8 @@ def _run_case(cfg, B, policy, k0, m, inp, dev, args, with_cpu):
         "pct_of_hbm_peak": round(100 * value / PEAK_HBM_GBPS, 2),
         "expert_ffn_us": round(ffn_ms * 1e3, 2),
         "roofline": {"bound": "hbm", "achieved": round(ffn_gbps, 1), "peak": PEAK_HBM_GBPS,
-                     "unit": "GB/s", "frac": round(ffn_gbps / PEAK_HBM_GBPS, 4), "traffic": None,
+                     "unit": "GB/s", "frac": round(ffn_gbps / PEAK_HBM_GBPS, 4),
+                     "traffic": _traffic(out_workload),
                      "kernel": "ffn_kernel (moe_expert_ffn: gate/up, SwiGLU, down and combine, one launch)",
                      "bytes_per_launch": c.active_bytes},
     }
@@ -236,6 +268,15 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    if args.copy_calibration:
+        n = int(args.copy_calibration * 1e6) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(10):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": n * 4, "copy_bytes_written": n * 4, "launches": 10}))
+        return
     if args.sweep:
         with open(args.sweep, "w") as f:
             for cname, cfg in CONFIGS.items():
@@ -257,6 +298,14 @@ def main():
     cfg = CONFIGS[args.config]
     inp = make_layer(cfg, max(args.batch, max(cfg.batches)))
     dev = _upload(inp, cfg.dtype)
+    if args.ffn_only:
+        c = Case(cfg, args.batch, args.policy, args.k0, args.m, inp, dev, args.rotate_bytes)
+        for i in range(args.ffn_only):
+            c.ffn(i % len(c.replicas))
+        torch.cuda.synchronize()
+        print(json.dumps({"ffn_launches": args.ffn_only, "n_active": c.n_active,
+                          "active_expert_bytes": c.active_bytes}), flush=True)
+        return
     rec = _run_case(cfg, args.batch, args.policy, args.k0, args.m, inp, dev, args,
                     with_cpu=not args.no_cpu_baseline)
     print(json.dumps(rec), flush=True)
