@@ -184,7 +184,7 @@ def _cpu_baseline(cfg, inp, B, policy, k0, m, active_bytes, seconds):
         t0 = time.perf_counter()
         orc.moe_layer(*args)
         times.append(time.perf_counter() - t0)
-        if time.perf_counter() > t_end or len(times) >= 50:
+        if time.perf_counter() > t_end or len(times) >= 200:
             break
     med = float(np.median(times))
     return {"value": active_bytes / med / 1e9, "unit": "GB/s", "cores": int(threads), "kind": "oracle",

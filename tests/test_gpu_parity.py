@@ -69,6 +69,21 @@ def _oracle(cfg, inp, B, policy, k0, m, tokens=None):
                          inp["w_down"], cfg.dtype, policy, cfg.k, k0, m, tokens=tokens)
 
 
+def _assert_routing_from_gpu_logits(Lg, rg, cfg, a):
+    """The oracle's selection run on the GPU's own float32 logits reproduces
+    the GPU routing bit for bit (budget ranks the GPU's batch masses, which
+    must match the oracle's masses of the same logits to 2e-6 relative)."""
+    if a["policy"] == "budget":
+        M = orc.budget_mass(Lg)
+        np.testing.assert_allclose(rg["mass"], M, rtol=2e-6, atol=1e-12, err_msg="batch_mass")
+        ids = orc.select_budget(Lg, cfg.k, a["m"], mass=rg["mass"])
+    else:
+        ids, _ = orc.select(Lg, a["policy"], cfg.k, a["k0"], a["m"])
+    o = {"ids": ids, "w": orc.gate_weights(Lg, ids)}
+    o.update(orc.compact(ids, cfg.E))
+    assert_routing_equal(rg, o, "oracle on GPU logits")
+
+
 def _layer_cases():
     cases = []
     for cname, cfg in CONFIGS.items():
@@ -97,6 +112,7 @@ def test_layer_matches_oracle(cname, B, policy, p):
     o = _oracle(cfg, inp, B, a["policy"], a["k0"], a["m"], tokens)
     assert_logits_close(Lg, o["logits"], cname)
     assert_routing_equal(rg, o, cname, weight_rtol_from_logits(Lg, o["logits"]))
+    _assert_routing_from_gpu_logits(Lg, rg, cfg, a)
     yg = y_to_f64(y)
     rows = slice(None) if tokens is None else tokens
     assert_y_close(yg[rows], o["y"][rows], cfg.dtype, f"{cname} B={B} {policy}{p}")
@@ -196,6 +212,10 @@ def test_select_matches_oracle(B, E, k, kind, policy, p):
     o.update(orc.compact(ids, E))
     if M is not None:
         np.testing.assert_allclose(g["mass"], M, rtol=2e-6, atol=1e-12, err_msg="batch_mass")
+        # Ranked on the GPU's own masses, the oracle's budget step must agree
+        # exactly (masses that differ only by rounding may order differently).
+        ids_g = orc.select_budget(Lh, k, a["m"], mass=g["mass"])
+        assert np.array_equal(g["ids"], ids_g), "budget set ranked on the GPU masses"
     assert_routing_equal(g, o, f"B{B} E{E} k{k} {kind} {policy}{p}")
 
 
