@@ -60,7 +60,9 @@ moe_status_t check_workspace(const void *ws, size_t have, size_t need) {
 // expert FFN's synchronisation words, so that a workspace can serve every
 // entry point.
 size_t route_bytes(int B, int d, int E) {
-  return router_offset(B, d) + align256(size_t(ceil_div(d, kRouterRows)) * B * E * sizeof(float));
+  const size_t tiles = size_t(ceil_div(E, kRouterTile)) * ceil_div(B, kRouterTile);
+  return router_offset(B, d) +
+         align256(tiles * ceil_div(d, kRouterRows) * kRouterTile * kRouterTile * sizeof(float));
 }
 
 #define MOE_TRY(expr)                     \
@@ -91,10 +93,10 @@ moe_status_t moe_route(const void *x, const void *w_g, const float *bias, moe_dt
   if (bias && !aligned(bias, 4)) return MOE_ERR_INVALID_ARG;
   MOE_TRY(check_workspace(workspace, workspace_bytes, route_bytes(B, d, E)));
   hipStream_t s = static_cast<hipStream_t>(stream);
-  float *part = reinterpret_cast<float *>(static_cast<char *>(workspace) + router_offset(B, d));
-  const int slices = ceil_div(d, kRouterRows);
-  MOE_TRY(hip_status(launch_router(x, w_g, dt, B, d, E, part, slices, s)));
-  return hip_status(launch_router_reduce(part, bias, slices, B, E, logits, s));
+  char *ws = static_cast<char *>(workspace);
+  float *part = reinterpret_cast<float *>(ws + router_offset(B, d));
+  uint32_t *cnt = reinterpret_cast<uint32_t *>(ws + kRouterCntOffset);
+  return hip_status(launch_router(x, w_g, bias, dt, B, d, E, part, cnt, logits, s));
 }
 
 moe_status_t moe_select(const float *logits, int B, int E, moe_policy_t policy,
@@ -149,8 +151,8 @@ moe_status_t moe_layer_decode(const void *x, const void *w_g, const float *bias,
   hipStream_t s = static_cast<hipStream_t>(stream);
   char *ws = static_cast<char *>(workspace);
   float *part = reinterpret_cast<float *>(ws + plan.router_part);
-  MOE_TRY(hip_status(launch_router(x, w_g, dt, B, d, E, part, plan.router_slices, s)));
-  MOE_TRY(hip_status(launch_router_reduce(part, bias, plan.router_slices, B, E, logits, s)));
+  uint32_t *cnt = reinterpret_cast<uint32_t *>(ws + plan.sync + kRouterCntOffset);
+  MOE_TRY(hip_status(launch_router(x, w_g, bias, dt, B, d, E, part, cnt, logits, s)));
   MOE_TRY(hip_status(launch_select(logits, B, E, policy, *routing, s)));
   return hip_status(launch_expert_ffn(x, w_gate, w_up, w_down, dt, B, d, E, I, policy.k, *routing,
                                       y, ws, plan, s));

@@ -16,8 +16,9 @@ constexpr int kMaxE = 256;
 constexpr int kMaxK = 16;
 constexpr int kMaxDim = 16384;
 
-// Router: rows of W_g per partial-sum slice.
-constexpr int kRouterRows = 32;
+// Router: rows of W_g per partial-sum slice; 16 x 16 logit tiles.
+constexpr int kRouterRows = 128;
+constexpr int kRouterTile = 16;
 
 // Expert FFN tiling (bf16 path). A work item is one active expert times one
 // strip of kStripCols output columns times one slice of the reduction.
@@ -32,7 +33,7 @@ inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
 struct Workspace {
   size_t sync;         // uint32 grid-barrier words of the expert FFN (kSyncBytes)
   size_t tok_cnt;      // uint32 [B][ceil(d/128)] per-(token, strip) counters of the expert FFN
-  size_t router_part;  // float [router_slices][B][E]
+  size_t router_part;  // float [tiles][router_slices][16 x 16] partial logit tiles
   size_t up_part;      // float [up_slices][2][B*k][I]   (gate, up partial sums)
   size_t h;            // bf16 or float [B*k][I]
   size_t down_part;    // float [B*k][d], one row per (expert, token) pair
@@ -45,11 +46,13 @@ struct Workspace {
 
 inline size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 
-// Bytes at the start of the workspace that hold the expert FFN's grid-barrier
-// words; its per-token counters follow. Both must be zero before the
-// workspace's first use; every call leaves them ready for the next one. No
-// other step writes them.
-constexpr size_t kSyncBytes = 512;
+// Bytes at the start of the workspace that hold synchronisation words: the
+// expert FFN's grid-barrier words (first 512 bytes), then the router's
+// per-tile counters (up to 256 tiles); the FFN's per-token counters follow.
+// All must be zero before the workspace's first use; every call leaves them
+// ready for the next one. No other step writes them.
+constexpr size_t kSyncBytes = 2048;
+constexpr size_t kRouterCntOffset = 512;
 
 // Offset of the router's partial sums: after the expert FFN's synchronisation
 // words (barrier words, then per-token counters), which depend on B and d only.
@@ -60,6 +63,7 @@ inline size_t router_offset(int B, int d) {
 inline Workspace plan_workspace(int B, int d, int E, int I, int k, moe_dtype_t dt) {
   Workspace w{};
   w.router_slices = ceil_div(d, kRouterRows);
+  const size_t router_tiles = size_t(ceil_div(E, kRouterTile)) * ceil_div(B, kRouterTile);
   int slices = ceil_div(d, kUpSliceMin);
   if (slices > kUpMaxSlices) slices = kUpMaxSlices;
   int rows = ceil_div(d, slices);
@@ -73,7 +77,7 @@ inline Workspace plan_workspace(int B, int d, int E, int I, int k, moe_dtype_t d
   w.tok_cnt = off + kSyncBytes;
   off = router_offset(B, d);
   w.router_part = off;
-  off = align256(off + size_t(w.router_slices) * B * E * sizeof(float));
+  off = align256(off + router_tiles * w.router_slices * kRouterTile * kRouterTile * sizeof(float));
   w.up_part = off;
   off = align256(off + size_t(w.up_slices) * 2 * P * I * sizeof(float));
   w.h = off;
@@ -89,10 +93,10 @@ inline Workspace plan_workspace(int B, int d, int E, int I, int k, moe_dtype_t d
 // ------------------------------------------------------------- launchers
 // Each launcher enqueues on `s` and returns hipGetLastError().
 
-hipError_t launch_router(const void *x, const void *w_g, moe_dtype_t dt, int B, int d, int E,
-                         float *part, int slices, hipStream_t s);
-hipError_t launch_router_reduce(const float *part, const float *bias, int slices, int B, int E,
-                                float *logits, hipStream_t s);
+// logits = x W_g + bias in one launch; part holds the partial tiles, cnt the
+// per-tile counters (zero before, zero after).
+hipError_t launch_router(const void *x, const void *w_g, const float *bias, moe_dtype_t dt, int B,
+                         int d, int E, float *part, uint32_t *cnt, float *logits, hipStream_t s);
 
 // Selection on float32 logits[B,E].
 hipError_t launch_select(const float *logits, int B, int E, moe_policy_t p,

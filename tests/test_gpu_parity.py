@@ -57,11 +57,13 @@ def _run_layer(cfg: LayerConfig, inp, dev, B: int, policy: str, k0: int, m: int,
 
 
 def _assert_sync_words_clear(ws):
-    """The FFN's grid-barrier count returns to zero and its error word stays
-    zero (a barrier wait never ran out)."""
-    words = ws[:512].view(torch.int32).cpu().numpy()
+    """The FFN's grid-barrier count returns to zero, its error word stays
+    zero (a barrier wait never ran out) and the router's tile counters are
+    back at zero."""
+    words = ws[:2048].view(torch.int32).cpu().numpy()
     assert words[0] == 0, f"barrier count left at {words[0]}"
     assert words[64] == 0, "a grid-barrier wait exceeded its bound"
+    assert not words[128:384].any(), "a router tile counter was left non-zero"
 
 
 def _oracle(cfg, inp, B, policy, k0, m, tokens=None):
