@@ -229,16 +229,16 @@ constexpr int kSyncErr = 64;
 constexpr uint32_t kSpinLimit = 1u << 20;
 
 // All workgroups of the grid (resident together: one per CU at most) meet
-// here. Every store a workgroup makes before the barrier and that others
-// read after it is a device-scope store, and those reads are device-scope
-// loads, so completing the stores before arriving (s_waitcnt vmcnt(0)) is
-// what orders them before the reads; no cache maintenance is needed. A wait
-// that does not end within kSpinLimit polls sets the error word and returns,
-// so the kernel always terminates.
-__device__ __forceinline__ void grid_barrier(uint32_t *sync) {
+// here; one wave of each workgroup takes part (its lanes wait for lane 0).
+// Every store that another workgroup reads after the barrier is a
+// device-scope store made before the arrival by a wave whose stores have
+// completed (s_waitcnt vmcnt(0)), and those reads are device-scope loads, so
+// no cache maintenance is needed. A wait that does not end within
+// kSpinLimit polls sets the error word and returns, so the kernel always
+// terminates.
+__device__ __forceinline__ void grid_barrier_wave(uint32_t *sync) {
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
-  if (threadIdx.x == 0) {
+  if ((threadIdx.x & 63) == 0) {
     uint32_t *count = sync + kSyncCount, *gen = sync + kSyncGen;
     const uint32_t g0 = __hip_atomic_load(gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     // The generation must be read before this workgroup's arrival can let
@@ -262,7 +262,6 @@ __device__ __forceinline__ void grid_barrier(uint32_t *sync) {
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   }
-  __syncthreads();
 }
 
 struct Params {
@@ -377,17 +376,15 @@ struct Stream {
     return (uint32_t(pr) * uint32_t(p.I) + kofs) * 2u;
   }
 
-  // The A-tile copies of stage c (MTX per wave). A down stage issued before
-  // h exists (h_ok false) copies x instead, a harmless stand-in that keeps
-  // the number of copies per stage fixed; its A tile is copied again once h
-  // is complete. h is read with device-scope copies (other workgroups wrote it).
-  __device__ __forceinline__ void issue_a(const Cursor &c, unsigned char *slot, bool h_ok) const {
+  // The A-tile copies of stage c (MTX per wave): x rows by token for gate/up,
+  // h rows by pair for down (device scope: other workgroups wrote h).
+  __device__ __forceinline__ void issue_a(const Cursor &c, unsigned char *slot) const {
     unsigned char *dst = slot + 2 * kWTile + wave * S::kXSub;
     const uint32_t xsoff = uint32_t(c.row0 + c.kst * kBK) * 2u;
-    if (c.up || !h_ok) {
+    if (c.up) {
       const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.x, uint32_t(p.B) * uint32_t(p.d) * 2u);
 #pragma unroll
-      for (int h = 0; h < MTX; ++h) dma16(ra, dst + h * 1024, c.up ? xvoff(c, h) : uint32_t(lane * 16), c.up ? xsoff : 0u);
+      for (int h = 0; h < MTX; ++h) dma16(ra, dst + h * 1024, xvoff(c, h), xsoff);
     } else {
       const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.h, uint32_t(p.P) * uint32_t(p.I) * 2u);
 #pragma unroll
@@ -395,8 +392,26 @@ struct Stream {
     }
   }
 
+  // The weight copies of down stage c that wave `vw` normally issues (4 per
+  // tile), issued by this wave: used while wave 0 is busy at the grid barriers.
+  __device__ __forceinline__ void issue_dn_weights_as(const Cursor &c, unsigned char *slot, int vw) const {
+    const size_t base = size_t(c.e) * p.I * p.d;
+    const __amdgpu_buffer_rsrc_t r = make_rsrc(p.W[2] + base, uint32_t(p.I) * uint32_t(p.d) * 2u);
+#pragma unroll
+    for (int mat = 0; mat < 2; ++mat) {
+      const uint32_t soff = (uint32_t(c.kst * kBK) * uint32_t(p.d) +
+                             uint32_t((2 * c.strip + mat) * kStripCols)) * 2u;
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        const int rr = 8 * (vw + 4 * h) + (lane >> 3);
+        const uint32_t voff = uint32_t(rr) * uint32_t(p.d) * 2u + uint32_t((lane & 7) ^ swz_w(rr)) * 16u;
+        dma16(r, slot + mat * kWTile + (vw + 4 * h) * 1024, voff, soff);
+      }
+    }
+  }
+
   // Issues every copy of stage c into `slot` (S::kCopies per wave).
-  __device__ __forceinline__ void issue(const Cursor &c, unsigned char *slot, bool h_ok) const {
+  __device__ __forceinline__ void issue(const Cursor &c, unsigned char *slot) const {
     if (c.up) {
       const size_t base = (size_t(c.e) * p.d + c.row0) * p.I;
       const uint32_t wbytes = uint32_t(c.nrows) * uint32_t(p.I) * 2u;
@@ -419,7 +434,7 @@ struct Stream {
         for (int h = 0; h < 4; ++h) dma16(r, slot + mat * kWTile + (wave + 4 * h) * 1024, wv_dn[h], soff);
       }
     }
-    issue_a(c, slot, h_ok);
+    issue_a(c, slot);
   }
 };
 
@@ -513,13 +528,13 @@ __device__ __forceinline__ void epilogue(const Cursor &c, const Params &p, uint3
     }
 }
 
-// h = SiLU(g) * u from the slice partial sums, spread over the whole grid.
-// All loads of a thread are issued before the first is used.
-__device__ __forceinline__ void h_phase(const Params &p, int total) {
+// h = SiLU(g) * u from the slice partial sums, spread over wave 0 of every
+// workgroup. All loads of a lane are issued before the first is used.
+__device__ __forceinline__ void h_phase_wave(const Params &p, int total) {
   const int q4 = p.I / 4;
   const int n = total * q4;
   const uint32_t blk = uint32_t(p.P) * uint32_t(p.I) * 4u;  // bytes of one [P][I] block
-  for (int idx = blockIdx.x * kThreads + threadIdx.x; idx < n; idx += gridDim.x * kThreads) {
+  for (int idx = blockIdx.x * 64 + (threadIdx.x & 63); idx < n; idx += gridDim.x * 64) {
     const int pr = idx / q4;
     const int c = (idx - pr * q4) * 4;
     const uint32_t off = (uint32_t(pr) * uint32_t(p.I) + uint32_t(c)) * 4u;
@@ -620,16 +635,55 @@ __device__ __forceinline__ void finish_down(const Cursor &c, const Params &p, un
   __syncthreads();
 }
 
+// The change from gate/up to down in a workgroup: every gate/up stage of it
+// has been consumed and no down stage issued (the producer stops at the first
+// one); `first` is the next stage index. Wave 0 meets the grid at the first
+// barrier (gate/up partial sums complete), forms its share of h and meets the
+// grid again (h complete); meanwhile waves 1-3 copy the weights of the next
+// kD down stages, wave 0's share included, so those copies overlap the
+// barriers without delaying wave 0's waits (vmcnt completes in order). Then
+// every wave copies its h rows of those stages and waits for all of them.
+template <int MTX>
+__device__ __forceinline__ void change_to_down(const Params &p, const Stream<MTX> &st, Cursor &prod,
+                                               int &issued, int first, unsigned char *stages,
+                                               int total) {
+  using S = Shape<2, MTX>;
+  constexpr int kS = S::kStages;
+  constexpr int kD = kS - 1;
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's gate/up stores
+  __syncthreads();
+  if (st.wave == 0) {
+    grid_barrier_wave(p.sync);
+    h_phase_wave(p, total);
+    grid_barrier_wave(p.sync);
+  } else {
+    Cursor q = prod;
+    for (int n = 0; n < kD && q.valid; ++n) {
+      unsigned char *slot = stages + ((first + n) % kS) * S::kSlot;
+      if (st.wave == 1) st.issue_dn_weights_as(q, slot, 0);
+      st.issue_dn_weights_as(q, slot, st.wave);
+      st.advance(q);
+    }
+  }
+  __syncthreads();
+  for (int n = 0; n < kD && prod.valid; ++n) {
+    st.issue_a(prod, stages + ((first + n) % kS) * S::kSlot);
+    st.advance(prod);
+    ++issued;
+  }
+  wait_barrier<0>();
+}
+
 // The whole bf16 expert FFN in one persistent kernel (one workgroup per CU,
 // all resident together):
 //   1. gate/up items stream G and U and store slice partial sums;
-//   2. grid barrier; h = SiLU(g) * u over the grid; grid barrier;
+//   2. grid barrier; h = SiLU(g) * u over the grid; grid barrier
+//      (change_to_down);
 //   3. down items stream D with h as the A operand and store rows by token
 //      slot; each token's strip of y is formed by the workgroup that
 //      completes it (finish_down).
-// The ring keeps copying across phases: the first down stages' weights are in
-// flight while the workgroup waits at the barriers; their A tiles are copied
-// once h is complete.
+// The first down stages' weights are in flight while the workgroup waits at
+// the grid barriers; their A tiles are copied once h is complete.
 template <int MTX>
 __global__ __launch_bounds__(kThreads, 1) void ffn_kernel(Params p,
                                                           const int32_t *__restrict__ n_active,
@@ -667,11 +721,12 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_kernel(Params p,
   st.decode(cons);
   Cursor prod = cons;
 
-  // Prologue: kD stages in flight. `issued` counts the stages issued so far.
+  // Prologue: kD stages in flight (gate/up only: down stages wait for h).
+  // `issued` counts the stages issued so far.
   int issued = 0;
   for (int s = 0; s < kD; ++s) {
-    if (!prod.valid) break;
-    st.issue(prod, stages + s * S::kSlot, false);
+    if (!prod.valid || !prod.up) break;
+    st.issue(prod, stages + s * S::kSlot);
     ++issued;
     st.advance(prod);
   }
@@ -682,18 +737,8 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_kernel(Params p,
   bool h_ready = false;
   for (int s = 0; cons.valid; ++s) {
     if (!cons.up && !h_ready) {
-      // This workgroup's gate/up stages are all done. The down stages already
-      // in the ring hold stand-in A tiles: copy their h rows now.
-      grid_barrier(p.sync);
-      h_phase(p, total);
-      grid_barrier(p.sync);
+      change_to_down<MTX>(p, st, prod, issued, s, stages, total);
       h_ready = true;
-      Cursor q = cons;
-      for (int t = s; t < issued; ++t) {
-        st.issue_a(q, stages + (t % kS) * S::kSlot, true);
-        st.advance(q);
-      }
-      wait_barrier<0>();
     }
     // Stage s must have landed; the stages issued after it may stay in flight
     // (S::kCopies copies per wave each).
@@ -705,8 +750,8 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_kernel(Params p,
       default: wait_barrier<(kD - 1 >= 3 ? 3 : 0) * S::kCopies>(); break;
     }
     // Every wave is past stage s-1, so its slot takes stage s+kD.
-    if (prod.valid) {
-      st.issue(prod, stages + ((s + kD) % kS) * S::kSlot, h_ready);
+    if (prod.valid && (prod.up || h_ready)) {
+      st.issue(prod, stages + ((s + kD) % kS) * S::kSlot);
       ++issued;
       st.advance(prod);
     }
@@ -718,11 +763,7 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_kernel(Params p,
     }
     st.advance(cons);
   }
-  if (!h_ready) {  // no down items here: still meet the grid twice
-    grid_barrier(p.sync);
-    h_phase(p, total);
-    grid_barrier(p.sync);
-  }
+  if (!h_ready) change_to_down<MTX>(p, st, prod, issued, 0, stages, total);  // no down items here
 }
 
 // ------------------------------------------------------------- combine (f32)
