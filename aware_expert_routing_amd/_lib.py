@@ -26,6 +26,7 @@ MOE_BF16 = 1
 MOE_POLICY_TOPK = 0
 MOE_POLICY_OEA = 1
 MOE_POLICY_BUDGET = 2
+MOE_POLICY_GREEDY = 3
 
 EXPORTS = ("moe_workspace_bytes", "moe_route", "moe_select", "moe_expert_ffn",
            "moe_layer_decode", "moe_status_string")
@@ -92,7 +93,8 @@ def _check(status: int):
 
 
 def make_policy(kind: str, k: int, k0: int = 0, m: int = 0) -> Policy:
-    kinds = {"topk": MOE_POLICY_TOPK, "oea": MOE_POLICY_OEA, "budget": MOE_POLICY_BUDGET}
+    kinds = {"topk": MOE_POLICY_TOPK, "oea": MOE_POLICY_OEA, "budget": MOE_POLICY_BUDGET,
+             "greedy": MOE_POLICY_GREEDY}
     if kind not in kinds:
         raise ValueError(f"unknown policy {kind!r}")
     return Policy(kinds[kind], int(k), int(k0), int(m))

@@ -30,6 +30,7 @@ moe_status_t check_policy(const moe_policy_t &p, int E) {
     case MOE_POLICY_OEA:
       return (p.k0 >= 1 && p.k0 <= p.k) ? MOE_OK : MOE_ERR_INVALID_ARG;
     case MOE_POLICY_BUDGET:
+    case MOE_POLICY_GREEDY:
       return (p.m >= 1 && p.m <= E) ? MOE_OK : MOE_ERR_INVALID_ARG;
     default:
       return MOE_ERR_INVALID_ARG;

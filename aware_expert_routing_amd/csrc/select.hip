@@ -10,6 +10,12 @@
 //   BUDGET(m) "XShare", abstract: maximise the total gating score. The batch
 //             mass of expert e is the sum over tokens of softmax(logits_t)[e];
 //             the m largest masses (ties to the lower index) form the set.
+//   GREEDY(m) "XShare", abstract (greedy solution): the set grows one expert
+//             at a time by the largest gain in retained mass
+//             F(S) = sum_t (sum of t's k largest probabilities inside S); the
+//             gain of e is sum_t max(0, p_t[e] - thr_t), thr_t being t's k-th
+//             largest probability in S (0 while t has fewer than k there);
+//             ties to the lower index.
 //   weights   softmax over each token's selected logits.
 //   compact   "Lynx", Technical Summary 2.2: the batch activates one
 //             consolidated expert set; this kernel lists it (ascending) and
@@ -114,6 +120,21 @@ __device__ __forceinline__ float wave_maxf(float v) {
   return __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(v), 63));
 }
 
+template <int CTRL, int ROWS>
+__device__ __forceinline__ float fmin_step(float v) {
+  return fminf(v, __uint_as_float(dpp<CTRL, ROWS>(__float_as_uint(v), __float_as_uint(v))));
+}
+
+__device__ __forceinline__ float wave_minf(float v) {
+  v = fmin_step<kDppQuadX1, 0xF>(v);
+  v = fmin_step<kDppQuadX2, 0xF>(v);
+  v = fmin_step<kDppHalfMirror, 0xF>(v);
+  v = fmin_step<kDppMirror, 0xF>(v);
+  v = fmin_step<kDppBcast15, 0xA>(v);
+  v = fmin_step<kDppBcast31, 0xC>(v);
+  return __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(v), 63));
+}
+
 // Up to `rounds` rounds of wave-wide argmax over the keys (expert lane+64v
 // holds key[v]). Lane r receives the r-th winner's expert and key; `top` is
 // the first winner's key. Returns the number of winners.
@@ -165,6 +186,11 @@ __global__ __launch_bounds__(kThreads) void select_kernel(
   __shared__ int apos[kMaxE];
   __shared__ int aoff[kMaxE];
   __shared__ int s_n, s_total;
+  __shared__ float tok_mx[kMaxB], tok_sm[kMaxB], tok_thr[kMaxB];  // GREEDY per-token state
+  __shared__ int tok_cnt[kMaxB];
+  __shared__ uint32_t w_best[kWaves];
+  __shared__ int w_e[kWaves];
+  __shared__ int s_pick;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -249,6 +275,131 @@ __global__ __launch_bounds__(kThreads) void select_kernel(
         rank += (o > macc) || (o == macc && e2 < tid);
       }
       if (rank < m) atomicOr(&allowed[tid >> 5], 1u << (tid & 31));
+    }
+  } else if (kind == MOE_POLICY_GREEDY) {
+    // Per-token softmax normalisers (probabilities are recomputed from the
+    // logits whenever needed, always by the same expression).
+#pragma unroll
+    for (int ti = 0; ti < kTokPerWave; ++ti) {
+      const int t = wave + kWaves * ti;
+      if (t < B) {
+        float mx = -INFINITY;
+#pragma unroll
+        for (int v = 0; v < NV; ++v)
+          if (lane + 64 * v < E) mx = fmaxf(mx, L[ti][v]);
+        mx = wave_maxf(mx);
+        float sm = 0.0f;
+#pragma unroll
+        for (int v = 0; v < NV; ++v)
+          if (lane + 64 * v < E) sm += expf(L[ti][v] - mx);
+        sm = wave_sum(sm);
+        if (lane == 0) {
+          tok_mx[t] = mx;
+          tok_sm[t] = sm;
+          tok_thr[t] = 0.0f;
+          tok_cnt[t] = 0;
+        }
+      }
+    }
+    uint64_t kept = 0;  // bit ti*NV+v: expert lane+64v is among token slot ti's k largest in S
+    __syncthreads();
+    for (int r = 0; r < m; ++r) {
+      // Gains over this wave's tokens, then over the waves in order.
+      float g[NV];
+#pragma unroll
+      for (int v = 0; v < NV; ++v) g[v] = 0.0f;
+#pragma unroll
+      for (int ti = 0; ti < kTokPerWave; ++ti) {
+        const int t = wave + kWaves * ti;
+        if (t < B) {
+          const float mx = tok_mx[t], sm = tok_sm[t], thr = tok_thr[t];
+#pragma unroll
+          for (int v = 0; v < NV; ++v) g[v] += fmaxf(0.0f, expf(L[ti][v] - mx) / sm - thr);
+        }
+      }
+#pragma unroll
+      for (int v = 0; v < NV; ++v) {
+        const int e = lane + 64 * v;
+        if (e < E) psum[wave][e] = g[v];
+      }
+      __syncthreads();
+      if (wave * 64 < E) {
+        uint32_t key = 0;  // 0: not a candidate
+        if (tid < E && !bit_of(allowed, tid)) {
+          float gain = 0.0f;
+          for (int w = 0; w < kWaves; ++w) gain += psum[w][tid];
+          key = ord_bits(gain);
+        }
+        const uint32_t best = wave_max_u32(key);
+        const unsigned long long b = __ballot(key == best && key != 0);
+        if (lane == 0) {
+          w_best[wave] = best;
+          w_e[wave] = b ? wave * 64 + __builtin_ctzll(b) : -1;
+        }
+      }
+      __syncthreads();
+      if (tid == 0) {
+        uint32_t best = 0;
+        int e = -1;
+        for (int w = 0; w * 64 < E; ++w)
+          if (w_e[w] >= 0 && w_best[w] > best) {
+            best = w_best[w];
+            e = w_e[w];
+          }
+        s_pick = e;
+        if (e >= 0) allowed[e >> 5] |= 1u << (e & 31);
+      }
+      __syncthreads();
+      const int e = s_pick;
+      if (e < 0) break;  // block-uniform: no expert left
+      // Token slots update their k largest probabilities inside S.
+      const int ve = e >> 6, le = e & 63;
+#pragma unroll
+      for (int ti = 0; ti < kTokPerWave; ++ti) {
+        const int t = wave + kWaves * ti;
+        if (t < B) {
+          const float mx = tok_mx[t], sm = tok_sm[t];
+          float pv[NV];
+#pragma unroll
+          for (int v = 0; v < NV; ++v) pv[v] = expf(L[ti][v] - mx) / sm;
+          float pe_l = 0.0f;
+#pragma unroll
+          for (int v = 0; v < NV; ++v)
+            if (v == ve) pe_l = pv[v];
+          const float pe = __shfl(pe_l, le);
+          int cnt = tok_cnt[t];
+          float thr = tok_thr[t];
+          bool changed = false;
+          if (cnt < k) {
+            if (lane == le) kept |= 1ull << (ti * NV + ve);
+            ++cnt;
+            changed = cnt == k;
+          } else if (pe > thr) {
+            // Drop one kept expert holding the threshold (the lowest index).
+            int drop = -1;
+#pragma unroll
+            for (int v = NV - 1; v >= 0; --v) {
+              const unsigned long long b =
+                  __ballot(((kept >> (ti * NV + v)) & 1ull) && pv[v] == thr);
+              if (b) drop = 64 * v + __builtin_ctzll(b);
+            }
+            if (lane == (drop & 63)) kept &= ~(1ull << (ti * NV + (drop >> 6)));
+            if (lane == le) kept |= 1ull << (ti * NV + ve);
+            changed = true;
+          }
+          if (changed) {
+            float mn = INFINITY;
+#pragma unroll
+            for (int v = 0; v < NV; ++v)
+              if ((kept >> (ti * NV + v)) & 1ull) mn = fminf(mn, pv[v]);
+            thr = wave_minf(mn);
+          }
+          if (lane == 0) {
+            tok_cnt[t] = cnt;
+            tok_thr[t] = thr;
+          }
+        }
+      }
     }
   }
   __syncthreads();

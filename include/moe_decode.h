@@ -19,7 +19,12 @@
  *                   BUDGET(m)  the m experts with the largest softmax mass
  *                              summed over the batch form the allowed set; each
  *                              token takes its top min(k,m) inside it ("XShare",
- *                              abstract: maximise the total gating score).
+ *                              abstract: maximise the total gating score);
+ *                   GREEDY(m)  the allowed set grows greedily, one expert at a
+ *                              time, by the largest gain in the batch's
+ *                              retained top-k softmax mass (ties to the lower
+ *                              index), m experts in all; each token takes its
+ *                              top min(k,m) inside it ("XShare", abstract).
  *   4. weights:   gate weights are the softmax over each token's selected
  *                 logits (renormalised); empty slots weigh 0.
  *   5. compaction: the ascending list of active experts and, per active
@@ -76,10 +81,11 @@ typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype_t;
 typedef enum {
   MOE_POLICY_TOPK = 0,   /* k experts per token (k <= E)                         */
   MOE_POLICY_OEA = 1,    /* 1 <= k0 <= k; tokens get min(k, |S|) experts         */
-  MOE_POLICY_BUDGET = 2  /* 1 <= m <= E; tokens get min(k, m) experts            */
+  MOE_POLICY_BUDGET = 2, /* 1 <= m <= E; tokens get min(k, m) experts            */
+  MOE_POLICY_GREEDY = 3  /* 1 <= m <= E; tokens get min(k, m) experts            */
 } moe_policy_kind_t;
 
-/* Selection policy. k0 is read only by OEA, m only by BUDGET. */
+/* Selection policy. k0 is read only by OEA, m only by BUDGET and GREEDY. */
 typedef struct {
   int32_t kind; /* moe_policy_kind_t */
   int32_t k;
@@ -100,7 +106,8 @@ typedef struct {
                                     ascending within an expert; then -1           */
   int32_t *pair_slot;      /* [B*k] slot j of that pair in topk_ids; then -1        */
   float *batch_mass;       /* [E]   BUDGET: sum over tokens of softmax(logits_t);
-                                    may be NULL (other policies leave it alone)   */
+                                    may be NULL (other policies, GREEDY included,
+                                    leave it alone)                               */
 } moe_routing_t;
 
 /* Bytes of workspace the calls below need for these sizes (256-byte aligned

@@ -217,9 +217,10 @@ def select_budget(L32: np.ndarray, k: int, m: int, mass=None) -> np.ndarray:
 def greedy_retained_set(L32: np.ndarray, k: int, m: int) -> np.ndarray:
     """Greedy maximisation of the retained top-k gating mass
     F(S) = sum_t (sum of token t's k largest probabilities inside S), one
-    expert at a time, [XShare] "greedy algorithms ... maximizing the total
-    gating score". Marginal gains are compared on float32-rounded values,
-    ties to the lower index (reading R2). Boolean mask [E].
+    expert at a time ([XShare] abstract: batch-aware selection solved
+    greedily for the largest total gating score). Marginal gains are compared
+    on float32-rounded values, ties to the lower index (reading R2).
+    Boolean mask [E].
 
     Pinned by: brute force on tiny inputs (1 - 1/e bound), and equality with
     budget(m) when m <= k (F is then modular on |S| <= k).

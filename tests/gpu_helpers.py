@@ -60,6 +60,8 @@ def policy_args(policy: str, p: int):
         return dict(policy="oea", k0=p, m=0)
     if policy == "budget":
         return dict(policy="budget", k0=0, m=p)
+    if policy == "greedy":
+        return dict(policy="greedy", k0=0, m=p)
     raise ValueError(policy)
 
 

@@ -96,6 +96,8 @@ def _layer(lib, **kw):
     (dict(pol=L.Policy(L.MOE_POLICY_BUDGET, 8, 0, 0)), L.MOE_ERR_INVALID_ARG),  # m < 1
     (dict(pol=L.Policy(L.MOE_POLICY_BUDGET, 8, 0, 129)), L.MOE_ERR_INVALID_ARG),  # m > E
     (dict(pol=L.Policy(L.MOE_POLICY_BUDGET, 8, 0, 32), r=_routing(mass=False)), L.MOE_ERR_INVALID_ARG),
+    (dict(pol=L.Policy(L.MOE_POLICY_GREEDY, 8, 0, 0)), L.MOE_ERR_INVALID_ARG),  # m < 1
+    (dict(pol=L.Policy(L.MOE_POLICY_GREEDY, 8, 0, 129)), L.MOE_ERR_INVALID_ARG),  # m > E
     (dict(pol=L.Policy(7, 8, 0, 0)), L.MOE_ERR_INVALID_ARG),
     (dict(ws=None), L.MOE_ERR_WORKSPACE),
     (dict(ws=A + 16), L.MOE_ERR_WORKSPACE),             # not 256-byte aligned
@@ -149,6 +151,9 @@ def test_select_validation(lib):
     bad.topk_w = A + 2
     assert call(r=bad) == L.MOE_ERR_INVALID_ARG
     assert call(pol=L.Policy(L.MOE_POLICY_BUDGET, 8, 0, 16), r=_routing(mass=False)) == L.MOE_ERR_INVALID_ARG
+    assert call(pol=L.Policy(L.MOE_POLICY_GREEDY, 8, 0, 0)) == L.MOE_ERR_INVALID_ARG
+    # GREEDY does not use batch_mass.
+    assert call(pol=L.Policy(L.MOE_POLICY_GREEDY, 8, 0, 0), r=_routing(mass=False)) == L.MOE_ERR_INVALID_ARG
 
 
 def test_ffn_validation(lib):

@@ -100,7 +100,14 @@ def _layer_cases():
 
 # ------------------------------------------------------------ whole layer
 
-@pytest.mark.parametrize("cname,B,policy,p", _layer_cases())
+def _greedy_layer_cases():
+    return [pytest.param(c, B, "greedy", m, id=f"{c}-B{B}-greedy{m}")
+            for c, B, m in (("tiny_f32", 4, 4), ("tiny_f32", 4, 8), ("lynx_bf16", 16, 24),
+                            ("qwen3_30b_bf16", 16, 24), ("qwen3_30b_bf16", 16, 32),
+                            ("specdec_bf16", 64, 32))]
+
+
+@pytest.mark.parametrize("cname,B,policy,p", _layer_cases() + _greedy_layer_cases())
 def test_layer_matches_oracle(cname, B, policy, p):
     cfg = CONFIGS[cname]
     inp, dev = _layer_inputs(cname)
@@ -183,10 +190,12 @@ _SEL_SHAPES = [(1, 128, 8), (4, 16, 4), (3, 8, 8), (16, 64, 8), (16, 128, 8), (6
                (37, 100, 6), (256, 256, 16), (128, 64, 1)]
 
 
-def _sel_policies(E, k):
+def _sel_policies(E, k, B):
     out = [("topk", 0)]
     out += [("oea", k0) for k0 in sorted({1, max(1, k // 2), k})]
     out += [("budget", m) for m in sorted({1, max(1, k - 1), max(1, E // 4), E})]
+    if B * E <= 64 * 128:  # the oracle's greedy re-sorts per candidate: keep it small
+        out += [("greedy", m) for m in sorted({1, max(1, k - 1), max(1, E // 4)})]
     return out
 
 
@@ -194,7 +203,7 @@ def _sel_cases():
     cases = []
     for (B, E, k) in _SEL_SHAPES:
         for kind in ("normal", "ties", "flat"):
-            for pol, p in _sel_policies(E, k):
+            for pol, p in _sel_policies(E, k, B):
                 cases.append(pytest.param(B, E, k, kind, pol, p, id=f"B{B}-E{E}-k{k}-{kind}-{pol}{p or ''}"))
     return cases
 
