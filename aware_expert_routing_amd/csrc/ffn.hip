@@ -27,7 +27,7 @@
 //   * A down pass counts its tokens on per-(token, strip) counters; the
 //     workgroup that completes a token's count forms y for that strip, adding
 //     the slots in order (no float atomics: results are reproducible).
-// float32 path (small layers): direct per-output dot products.
+// float32 path (small layers): plain dot products, 16 row groups per column.
 #include "moe_internal.h"
 
 namespace moe {
@@ -793,47 +793,80 @@ __global__ __launch_bounds__(kThreads) void combine_f32_kernel(const float *__re
 }
 
 // ----------------------------------------------------------- float32 path
-// One thread per (pair, column of I): h = SiLU(x G) * (x U), float32.
-__global__ __launch_bounds__(kThreads) void up_f32_kernel(
+// Small layers. A 1024-thread workgroup owns one (pair, 64-column block):
+// row group r (16 of them) adds rows r, r+16, ... of each column with
+// coalesced row loads; the 16 partial sums are then added in order.
+constexpr int kF32Threads = 1024;
+constexpr int kF32Cols = 64;
+constexpr int kF32Groups = kF32Threads / kF32Cols;
+
+// grid = (ceil(I/64), B*k): h[pair] = SiLU(x G) * (x U).
+__global__ __launch_bounds__(kF32Threads) void up_f32_kernel(
     const float *__restrict__ x, const float *__restrict__ wg, const float *__restrict__ wu, int d,
     int I, int k, const int32_t *__restrict__ n_active, const int32_t *__restrict__ offsets,
     const int32_t *__restrict__ pair_token, const int32_t *__restrict__ pair_slot,
     const int32_t *__restrict__ topk_ids, float *__restrict__ h, int32_t *__restrict__ pair_of_slot) {
-  const int total = offsets[n_active[0]];
-  const int idx = blockIdx.x * kThreads + threadIdx.x;
-  if (idx >= total * I) return;
-  const int pr = idx / I, c = idx - pr * I;
+  __shared__ float red[2][kF32Groups][kF32Cols];
+  const int pr = blockIdx.y;
+  if (pr >= offsets[n_active[0]]) return;  // whole workgroup
+  const int tx = threadIdx.x % kF32Cols, ty = threadIdx.x / kF32Cols;
+  const int c = blockIdx.x * kF32Cols + tx;
   const int t = pair_token[pr];
-  const int e = topk_ids[t * k + pair_slot[pr]];
-  if (c == 0) pair_of_slot[t * k + pair_slot[pr]] = pr;
-  const float *xr = x + size_t(t) * d;
-  const float *G = wg + size_t(e) * d * I + c;
-  const float *U = wu + size_t(e) * d * I + c;
+  const int slot = t * k + pair_slot[pr];
+  const int e = topk_ids[slot];
+  if (blockIdx.x == 0 && threadIdx.x == 0) pair_of_slot[slot] = pr;
   float g = 0.f, u = 0.f;
-  for (int i = 0; i < d; ++i) {
-    g = fmaf(xr[i], G[size_t(i) * I], g);
-    u = fmaf(xr[i], U[size_t(i) * I], u);
+  if (c < I) {
+    const float *xr = x + size_t(t) * d;
+    const float *G = wg + size_t(e) * d * I + c;
+    const float *U = wu + size_t(e) * d * I + c;
+#pragma unroll 4
+    for (int i = ty; i < d; i += kF32Groups) {
+      g = fmaf(xr[i], G[size_t(i) * I], g);
+      u = fmaf(xr[i], U[size_t(i) * I], u);
+    }
   }
-  h[size_t(pr) * I + c] = silu(g) * u;
+  red[0][ty][tx] = g;
+  red[1][ty][tx] = u;
+  __syncthreads();
+  if (ty == 0 && c < I) {
+    float gs = 0.f, us = 0.f;
+#pragma unroll
+    for (int r = 0; r < kF32Groups; ++r) {
+      gs += red[0][r][tx];
+      us += red[1][r][tx];
+    }
+    h[size_t(pr) * I + c] = silu(gs) * us;
+  }
 }
 
-// One thread per (pair, column of d): part[pair] = h D, float32.
-__global__ __launch_bounds__(kThreads) void down_f32_kernel(
+// grid = (ceil(d/64), B*k): part[pair] = h D.
+__global__ __launch_bounds__(kF32Threads) void down_f32_kernel(
     const float *__restrict__ h, const float *__restrict__ wd, int d, int I, int k,
     const int32_t *__restrict__ n_active, const int32_t *__restrict__ offsets,
     const int32_t *__restrict__ pair_token, const int32_t *__restrict__ pair_slot,
     const int32_t *__restrict__ topk_ids, float *__restrict__ part) {
-  const int total = offsets[n_active[0]];
-  const int idx = blockIdx.x * kThreads + threadIdx.x;
-  if (idx >= total * d) return;
-  const int pr = idx / d, c = idx - pr * d;
-  const int slot = pair_token[pr] * k + pair_slot[pr];
-  const int e = topk_ids[slot];
-  const float *hr = h + size_t(pr) * I;
-  const float *D = wd + size_t(e) * I * d + c;
+  __shared__ float red[kF32Groups][kF32Cols];
+  const int pr = blockIdx.y;
+  if (pr >= offsets[n_active[0]]) return;  // whole workgroup
+  const int tx = threadIdx.x % kF32Cols, ty = threadIdx.x / kF32Cols;
+  const int c = blockIdx.x * kF32Cols + tx;
+  const int e = topk_ids[pair_token[pr] * k + pair_slot[pr]];
   float acc = 0.f;
-  for (int i = 0; i < I; ++i) acc = fmaf(hr[i], D[size_t(i) * d], acc);
-  part[size_t(pr) * d + c] = acc;
+  if (c < d) {
+    const float *hr = h + size_t(pr) * I;
+    const float *D = wd + size_t(e) * I * d + c;
+#pragma unroll 4
+    for (int i = ty; i < I; i += kF32Groups) acc = fmaf(hr[i], D[size_t(i) * d], acc);
+  }
+  red[ty][tx] = acc;
+  __syncthreads();
+  if (ty == 0 && c < d) {
+    float s = 0.f;
+#pragma unroll
+    for (int r = 0; r < kF32Groups; ++r) s += red[r][tx];
+    part[size_t(pr) * d + c] = s;
+  }
 }
 
 int device_cus() {
@@ -904,11 +937,11 @@ hipError_t launch_expert_ffn(const void *x, const void *w_gate, const void *w_up
       launch_ffn<4>(grid, p, r, s);
   } else {
     float *h = reinterpret_cast<float *>(ws + plan.h);
-    up_f32_kernel<<<ceil_div(P * I, kThreads), kThreads, 0, s>>>(
+    up_f32_kernel<<<dim3(ceil_div(I, kF32Cols), P), kF32Threads, 0, s>>>(
         static_cast<const float *>(x), static_cast<const float *>(w_gate),
         static_cast<const float *>(w_up), d, I, k, r.n_active, r.expert_offsets, r.pair_token,
         r.pair_slot, r.topk_ids, h, pos);
-    down_f32_kernel<<<ceil_div(P * d, kThreads), kThreads, 0, s>>>(
+    down_f32_kernel<<<dim3(ceil_div(d, kF32Cols), P), kF32Threads, 0, s>>>(
         h, static_cast<const float *>(w_down), d, I, k, r.n_active, r.expert_offsets,
         r.pair_token, r.pair_slot, r.topk_ids, part);
     combine_f32_kernel<<<ceil_div(B * (d / 4), kThreads), kThreads, 0, s>>>(
