@@ -151,10 +151,15 @@ moe_status_t moe_layer_decode(const void *x, const void *w_g, const float *bias,
   MOE_TRY(check_workspace(workspace, workspace_bytes, plan.total));
   hipStream_t s = static_cast<hipStream_t>(stream);
   char *ws = static_cast<char *>(workspace);
-  float *part = reinterpret_cast<float *>(ws + plan.router_part);
-  uint32_t *cnt = reinterpret_cast<uint32_t *>(ws + plan.sync + kRouterCntOffset);
-  MOE_TRY(hip_status(launch_router(x, w_g, bias, dt, B, d, E, part, cnt, logits, s)));
-  MOE_TRY(hip_status(launch_select(logits, B, E, policy, *routing, s)));
+  if (dt == MOE_BF16) {
+    uint32_t *cnt = reinterpret_cast<uint32_t *>(ws + plan.sync + kRouteSelectCntOffset);
+    MOE_TRY(hip_status(launch_route_select(x, w_g, bias, B, d, E, logits, cnt, policy, *routing, s)));
+  } else {
+    float *part = reinterpret_cast<float *>(ws + plan.router_part);
+    uint32_t *cnt = reinterpret_cast<uint32_t *>(ws + plan.sync + kRouterCntOffset);
+    MOE_TRY(hip_status(launch_router(x, w_g, bias, dt, B, d, E, part, cnt, logits, s)));
+    MOE_TRY(hip_status(launch_select(logits, B, E, policy, *routing, s)));
+  }
   return hip_status(launch_expert_ffn(x, w_gate, w_up, w_down, dt, B, d, E, I, policy.k, *routing,
                                       y, ws, plan, s));
 }

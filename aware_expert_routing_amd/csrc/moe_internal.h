@@ -52,6 +52,7 @@ inline size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 // All must be zero before the workspace's first use; every call leaves them
 // ready for the next one. No other step writes them.
 constexpr size_t kSyncBytes = 2048;
+constexpr size_t kRouteSelectCntOffset = 384;  // fused router + selection: tiles done
 constexpr size_t kRouterCntOffset = 512;
 
 // Offset of the router's partial sums: after the expert FFN's synchronisation
@@ -101,6 +102,12 @@ hipError_t launch_router(const void *x, const void *w_g, const float *bias, moe_
 // Selection on float32 logits[B,E].
 hipError_t launch_select(const float *logits, int B, int E, moe_policy_t p,
                          const moe_routing_t &r, hipStream_t s);
+
+// bf16 router and selection in one launch; cnt is a counter word (zero before,
+// zero after).
+hipError_t launch_route_select(const void *x, const void *w_g, const float *bias, int B, int d,
+                               int E, float *logits, uint32_t *cnt, moe_policy_t p,
+                               const moe_routing_t &r, hipStream_t s);
 
 hipError_t launch_expert_ffn(const void *x, const void *w_gate, const void *w_up,
                              const void *w_down, moe_dtype_t dt, int B, int d, int E, int I,

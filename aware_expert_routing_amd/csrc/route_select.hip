@@ -1,0 +1,67 @@
+// Router and selection in one launch (bf16 layers, moe_layer_decode).
+// Each 1024-thread workgroup computes one 16 x 16 tile of the logits
+// (router_tile) and stores it with device-scope stores; it then counts itself
+// on a counter in the workspace. The workgroup that completes the count runs
+// the whole selection (select_block) on the finished logits and resets the
+// counter. The logits are bit-identical to moe_route's, and the routing to
+// moe_select's on them.
+#include "router_impl.h"
+#include "select_impl.h"
+
+namespace moe {
+namespace {
+
+static_assert(kRtThreads == kThreads, "router tile and selection share the workgroup size");
+
+template <bool VEC, int NV, int TPW>
+__global__ __launch_bounds__(kThreads) void route_select_kernel(
+    const uint16_t *__restrict__ x, const uint16_t *__restrict__ w, const float *__restrict__ bias,
+    int B, int d, int E, float *__restrict__ logits, uint32_t *__restrict__ cnt, int kind, int k,
+    int k0, int m, int32_t *__restrict__ topk_ids, float *__restrict__ topk_w,
+    int32_t *__restrict__ n_active, int32_t *__restrict__ active_experts,
+    int32_t *__restrict__ expert_offsets, int32_t *__restrict__ pair_token,
+    int32_t *__restrict__ pair_slot, float *__restrict__ batch_mass) {
+  __shared__ RouterLds sm;
+  __shared__ int s_last;
+  router_tile<VEC>(x, w, bias, B, d, E, logits, sm);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this tile's logits are stored
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const uint32_t before =
+        __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    s_last = before == gridDim.x * gridDim.y - 1;
+    if (s_last) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __syncthreads();
+  if (!s_last) return;
+  select_block<NV, TPW>(logits, B, E, kind, k, k0, m, topk_ids, topk_w, n_active, active_experts,
+                   expert_offsets, pair_token, pair_slot, batch_mass);
+}
+
+template <bool VEC>
+void launch_rs(dim3 grid, const uint16_t *x, const uint16_t *w, const float *bias, int B, int d,
+               int E, float *logits, uint32_t *cnt, const moe_policy_t &p, const moe_routing_t &r,
+               hipStream_t s) {
+  float *mass = p.kind == MOE_POLICY_BUDGET ? r.batch_mass : nullptr;
+  dispatch_select_shape(B, E, [&](auto nv, auto tpw) {
+    route_select_kernel<VEC, decltype(nv)::value, decltype(tpw)::value><<<grid, kThreads, 0, s>>>(
+        x, w, bias, B, d, E, logits, cnt, p.kind, p.k, p.k0, p.m, r.topk_ids, r.topk_w,
+        r.n_active, r.active_experts, r.expert_offsets, r.pair_token, r.pair_slot, mass);
+  });
+}
+
+}  // namespace
+
+hipError_t launch_route_select(const void *x, const void *w_g, const float *bias, int B, int d,
+                               int E, float *logits, uint32_t *cnt, moe_policy_t p,
+                               const moe_routing_t &r, hipStream_t s) {
+  const dim3 grid(ceil_div(E, kRtTile), ceil_div(B, kRtTile));
+  const uint16_t *xb = static_cast<const uint16_t *>(x), *wb = static_cast<const uint16_t *>(w_g);
+  if (E % kRtTile == 0)
+    launch_rs<true>(grid, xb, wb, bias, B, d, E, logits, cnt, p, r, s);
+  else
+    launch_rs<false>(grid, xb, wb, bias, B, d, E, logits, cnt, p, r, s);
+  return hipGetLastError();
+}
+
+}  // namespace moe

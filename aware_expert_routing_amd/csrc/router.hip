@@ -2,128 +2,24 @@
 // ("Router Caching and Optimization", section "Analyzing Router Inference
 // Cost", step 1). W_g is [d, E], contiguous along E.
 //
-// bf16: one workgroup per 16-token x 16-expert tile of the logits, over the
-// whole reduction, on MFMA (v_mfma_f32_16x16x32_bf16). The four waves take a
-// quarter of the reduction each; A fragments (8 consecutive features of one
-// token) load straight from x; W_g's 16 columns are staged in LDS in blocks
-// of 128 rows (16-byte loads) and read back as B fragments (8 consecutive
-// rows of one column). The waves' partial tiles are added in wave order, then
-// the bias: the logits are the same bits on every run.
+// bf16: one 1024-thread workgroup per 16-token x 16-expert tile of the
+// logits, over the whole reduction, on MFMA (router_tile in router_impl.h).
 //
-// float32 (small layers): a workgroup owns a 16-token x 16-expert tile of the logits and
-// one slice of kRouterRows rows of the reduction: it stages its slice of x and
-// of W_g in LDS (as float32, 16-byte loads where the rows allow), forms the
-// 256 float32 dot products, and stores them as the slice's partial tile. It
-// then counts itself on the tile's counter; the workgroup that completes the
-// count adds the bias and the slices' partial tiles in slice order (so the
-// logits are the same bits on every run), writes them and resets the counter.
-// The reduction is split over many workgroups because the product is tiny and
-// latency-bound: at d = 2048, E = 128, B = 16 it is 128 workgroups reading
-// 8 KB each.
-#include "moe_internal.h"
+// float32 (small layers): a workgroup owns a 16-token x 16-expert tile of
+// the logits and one slice of kRouterRows rows of the reduction: it stages
+// its slice of x and of W_g in LDS (16-byte loads where the rows allow),
+// forms the 256 float32 dot products, and stores them as the slice's partial
+// tile. It then counts itself on the tile's counter; the workgroup that
+// completes the count adds the bias and the slices' partial tiles in slice
+// order (so the logits are the same bits on every run), writes them and
+// resets the counter.
+#include "router_impl.h"
 
 namespace moe {
 namespace {
 
 constexpr int kThreads = 256;
 constexpr int kTile = 16;  // tokens and experts per tile
-
-typedef short bf16x8_t __attribute__((__vector_size__(8 * sizeof(short))));
-typedef float f32x4_t __attribute__((__vector_size__(4 * sizeof(float))));
-
-constexpr int kBlockRows = 128;               // W_g rows per LDS block (4 k-steps)
-constexpr int kGroupBlocks = 4;               // blocks whose loads are issued together
-
-// grid = (ceil(E/16), ceil(B/16)); block = 256 (4 waves). VEC: the tile's 16
-// columns are 16-byte aligned in every row (E % 8 == 0 and a whole tile).
-template <bool VEC>
-__global__ __launch_bounds__(kThreads) void router_mfma_kernel(
-    const uint16_t *__restrict__ x, const uint16_t *__restrict__ w, const float *__restrict__ bias,
-    int B, int d, int E, float *__restrict__ logits) {
-  __shared__ uint16_t wl[4][kGroupBlocks][kBlockRows][kTile];  // per wave: W_g rows x 16 columns
-  __shared__ float red[4][kTile][kTile];
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int j = lane & 15, g = lane >> 4;
-  const int e0 = blockIdx.x * kTile, t0 = blockIdx.y * kTile;
-  const int ne = min(kTile, E - e0);
-  const int tok = min(t0 + j, B - 1);  // clamped: rows past B are computed and dropped
-  // This wave's k-steps (32 reduction rows each).
-  const int nks = (d + 31) / 32;
-  const int per = (nks + 3) / 4;
-  const int ks0 = wave * per, ks1 = min(nks, ks0 + per);
-  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-  for (int kb = ks0; kb < ks1; kb += 4 * kGroupBlocks) {
-    // Issue every load of up to kGroupBlocks blocks, then use them.
-    bf16x8_t a[4 * kGroupBlocks];
-    uint4 wv[kGroupBlocks][4];
-    bool wok[kGroupBlocks][4];
-#pragma unroll
-    for (int q = 0; q < 4 * kGroupBlocks; ++q) {
-      const int k = (kb + q) * 32 + 8 * g;
-      // Features past d (or of k-steps this wave does not use) read feature 0:
-      // any finite value does, the W_g rows they meet are zero.
-      const int kk = (kb + q < ks1 && k < d) ? k : 0;
-      a[q] = *reinterpret_cast<const bf16x8_t *>(x + size_t(tok) * d + kk);
-    }
-#pragma unroll
-    for (int b = 0; b < kGroupBlocks; ++b) {
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int piece = lane + 64 * q;  // 256 pieces of 16 B: row piece/2, half piece%2
-        const int row = (kb + 4 * b) * 32 + piece / 2;
-        const int c0 = (piece & 1) * 8;
-        // Rows past d or outside this wave's range read row 0 (every load stays
-        // in bounds and is issued unconditionally) and are stored as zero.
-        const bool ok = kb + 4 * b < ks1 && row < d;
-        wok[b][q] = ok;
-        const size_t ro = size_t(ok ? row : 0) * E + e0 + c0;
-        if (VEC) {
-          wv[b][q] = *reinterpret_cast<const uint4 *>(w + ro);
-        } else {
-          uint32_t t[4];
-#pragma unroll
-          for (int c = 0; c < 4; ++c) {
-            const uint32_t lo = (c0 + 2 * c < ne) ? w[ro + 2 * c] : 0u;
-            const uint32_t hi = (c0 + 2 * c + 1 < ne) ? w[ro + 2 * c + 1] : 0u;
-            t[c] = lo | (hi << 16);
-          }
-          wv[b][q] = make_uint4(t[0], t[1], t[2], t[3]);
-        }
-      }
-    }
-#pragma unroll
-    for (int b = 0; b < kGroupBlocks; ++b)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int piece = lane + 64 * q;
-        *reinterpret_cast<uint4 *>(&wl[wave][b][piece / 2][(piece & 1) * 8]) =
-            wok[b][q] ? wv[b][q] : make_uint4(0, 0, 0, 0);
-      }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-#pragma unroll
-    for (int q = 0; q < 4 * kGroupBlocks; ++q) {
-      if (kb + q < ks1) {
-        bf16x8_t bfrag;
-#pragma unroll
-        for (int r = 0; r < 8; ++r) bfrag[r] = short(wl[wave][q / 4][(q % 4) * 32 + 8 * g + r][j]);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[q], bfrag, acc, 0, 0, 0);
-      }
-    }
-    __builtin_amdgcn_wave_barrier();
-  }
-  // acc holds rows 4g + i (tokens), column j (expert) of this wave's partial tile.
-#pragma unroll
-  for (int i = 0; i < 4; ++i) red[wave][4 * g + i][j] = acc[i];
-  __syncthreads();
-  const int ti = threadIdx.x / kTile, ej = threadIdx.x % kTile;
-  if (t0 + ti < B && ej < ne) {
-    float v = bias ? bias[e0 + ej] : 0.0f;
-    v += red[0][ti][ej] + red[1][ti][ej] + red[2][ti][ej] + red[3][ti][ej];
-    logits[size_t(t0 + ti) * E + e0 + ej] = v;
-  }
-}
 
 template <typename T>
 __device__ __forceinline__ float to_f32(T v);
@@ -161,6 +57,15 @@ __device__ __forceinline__ void stage(const T *__restrict__ src, size_t ld, int 
       dst[r * dld + c] = (r < nr && c < nc) ? to_f32<T>(src[size_t(r) * ld + c]) : 0.0f;
     }
   }
+}
+
+// bf16: grid = (ceil(E/16), ceil(B/16)); block = 1024.
+template <bool VEC>
+__global__ __launch_bounds__(kRtThreads) void router_mfma_kernel(
+    const uint16_t *__restrict__ x, const uint16_t *__restrict__ w, const float *__restrict__ bias,
+    int B, int d, int E, float *__restrict__ logits) {
+  __shared__ RouterLds sm;
+  router_tile<VEC>(x, w, bias, B, d, E, logits, sm);
 }
 
 // float32: grid = (ceil(E/16), slices, ceil(B/16)); block = 256 = 16 x 16
@@ -217,9 +122,9 @@ hipError_t launch_router(const void *x, const void *w_g, const float *bias, moe_
     const dim3 grid(ceil_div(E, kTile), ceil_div(B, kTile));
     const uint16_t *xb = static_cast<const uint16_t *>(x), *wb = static_cast<const uint16_t *>(w_g);
     if (E % kTile == 0)
-      router_mfma_kernel<true><<<grid, kThreads, 0, s>>>(xb, wb, bias, B, d, E, logits);
+      router_mfma_kernel<true><<<grid, kRtThreads, 0, s>>>(xb, wb, bias, B, d, E, logits);
     else
-      router_mfma_kernel<false><<<grid, kThreads, 0, s>>>(xb, wb, bias, B, d, E, logits);
+      router_mfma_kernel<false><<<grid, kRtThreads, 0, s>>>(xb, wb, bias, B, d, E, logits);
     return hipGetLastError();
   }
   dim3 grid(ceil_div(E, kTile), ceil_div(d, kRouterRows), ceil_div(B, kTile));

@@ -1,0 +1,532 @@
+#pragma once
+#include <type_traits>
+// Ranking, batch re-route, gate weights and compaction, in one workgroup
+// (device function select_block; used by select.hip and route_select.hip).
+//
+//   ranking   "Router Caching and Optimization", "Analyzing Router Inference
+//             Cost", steps 2-3: softmax and top-k; experts are ranked by
+//             logit (softmax is increasing), ties to the lower index, and
+//             -0.0 ranks equal to +0.0.
+//   OEA(k0)   "Opportunistic Expert Activation", abstract: tokens keep their
+//             top-k0; S = union over the batch; each token then fills up to k
+//             slots with its best experts inside S.
+//   BUDGET(m) "XShare", abstract: maximise the total gating score. The batch
+//             mass of expert e is the sum over tokens of softmax(logits_t)[e];
+//             the m largest masses (ties to the lower index) form the set.
+//   GREEDY(m) "XShare", abstract (greedy solution): the set grows one expert
+//             at a time by the largest gain in retained mass
+//             F(S) = sum_t (sum of t's k largest probabilities inside S); the
+//             gain of e is sum_t max(0, p_t[e] - thr_t), thr_t being t's k-th
+//             largest probability in S (0 while t has fewer than k there);
+//             ties to the lower index.
+//   weights   softmax over each token's selected logits.
+//   compact   "Lynx", Technical Summary 2.2: the batch activates one
+//             consolidated expert set; this kernel lists it (ascending) and
+//             the tokens of each active expert (ascending).
+//
+// Work split: the batch step couples all tokens, so one workgroup of 16 waves
+// does everything. Wave w owns tokens w, w+16, ...; lane l owns experts l,
+// l+64, ... (NV = ceil(E/64) of them). A token's experts are ranked by
+// repeated wave-wide maxima of order-preserving 32-bit keys; among equal keys
+// the lowest expert index is read off the ballots of "key == max" (scalar
+// work). Key 0 is no finite logit's key and marks "not a candidate".
+//
+// Results stay in LDS until the last phase: per (token, slot) the expert and
+// weight, per expert a bitmask of its tokens. The position of token t in
+// expert e's list is then the number of lower tokens in that bitmask, so the
+// pair lists are written by all threads at once.
+#include "moe_internal.h"
+
+namespace moe {
+namespace {
+
+constexpr int kThreads = 1024;
+constexpr int kWaves = kThreads / 64;
+constexpr int kMaxTokPerWave = kMaxB / kWaves;  // token slots per wave at B = 256
+constexpr int kWords = kMaxE / 32;           // words of an expert bitmask
+constexpr int kTokWords = kMaxB / 32;        // words of a token bitmask
+
+// Total order on float32 as unsigned integers; -0.0 maps like +0.0.
+__device__ __forceinline__ uint32_t ord_bits(float v) {
+  uint32_t u = __float_as_uint(v);
+  if ((u & 0x7FFFFFFFu) == 0) u = 0;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ float from_ord_bits(uint32_t o) {
+  return __uint_as_float((o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o);
+}
+
+// Wave-wide reductions with DPP lane moves (gfx9 encodings): quad_perm
+// [1,0,3,2] and [2,3,0,1], row_half_mirror, row_mirror, then row_bcast:15
+// into rows 1 and 3 and row_bcast:31 into rows 2 and 3. After the six steps
+// lane 63 holds the result over all 64 lanes; readlane makes it uniform.
+constexpr int kDppQuadX1 = 0xB1;
+constexpr int kDppQuadX2 = 0x4E;
+constexpr int kDppHalfMirror = 0x141;
+constexpr int kDppMirror = 0x140;
+constexpr int kDppBcast15 = 0x142;
+constexpr int kDppBcast31 = 0x143;
+
+// Lanes that a step does not write keep `old`.
+template <int CTRL, int ROWS>
+__device__ __forceinline__ uint32_t dpp(uint32_t old, uint32_t v) {
+  return uint32_t(__builtin_amdgcn_update_dpp(int(old), int(v), CTRL, ROWS, 0xF, false));
+}
+
+template <int CTRL, int ROWS>
+__device__ __forceinline__ uint32_t umax_step(uint32_t v) {
+  const uint32_t w = dpp<CTRL, ROWS>(v, v);
+  return w > v ? w : v;
+}
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = umax_step<kDppQuadX1, 0xF>(v);
+  v = umax_step<kDppQuadX2, 0xF>(v);
+  v = umax_step<kDppHalfMirror, 0xF>(v);
+  v = umax_step<kDppMirror, 0xF>(v);
+  v = umax_step<kDppBcast15, 0xA>(v);
+  v = umax_step<kDppBcast31, 0xC>(v);
+  return __builtin_amdgcn_readlane(v, 63);
+}
+
+// Sum over the wave in a fixed tree; every lane gets the lane-63 result, so
+// the value is uniform and reproducible from run to run.
+template <int CTRL, int ROWS>
+__device__ __forceinline__ float add_step(float v) {
+  // Lanes outside ROWS receive 0 (old) and keep their value.
+  return v + __uint_as_float(dpp<CTRL, ROWS>(0u, __float_as_uint(v)));
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+  v = add_step<kDppQuadX1, 0xF>(v);
+  v = add_step<kDppQuadX2, 0xF>(v);
+  v = add_step<kDppHalfMirror, 0xF>(v);
+  v = add_step<kDppMirror, 0xF>(v);
+  v = add_step<kDppBcast15, 0xA>(v);
+  v = add_step<kDppBcast31, 0xC>(v);
+  return __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(v), 63));
+}
+
+template <int CTRL, int ROWS>
+__device__ __forceinline__ float fmax_step(float v) {
+  return fmaxf(v, __uint_as_float(dpp<CTRL, ROWS>(__float_as_uint(v), __float_as_uint(v))));
+}
+
+__device__ __forceinline__ float wave_maxf(float v) {
+  v = fmax_step<kDppQuadX1, 0xF>(v);
+  v = fmax_step<kDppQuadX2, 0xF>(v);
+  v = fmax_step<kDppHalfMirror, 0xF>(v);
+  v = fmax_step<kDppMirror, 0xF>(v);
+  v = fmax_step<kDppBcast15, 0xA>(v);
+  v = fmax_step<kDppBcast31, 0xC>(v);
+  return __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(v), 63));
+}
+
+template <int CTRL, int ROWS>
+__device__ __forceinline__ float fmin_step(float v) {
+  return fminf(v, __uint_as_float(dpp<CTRL, ROWS>(__float_as_uint(v), __float_as_uint(v))));
+}
+
+__device__ __forceinline__ float wave_minf(float v) {
+  v = fmin_step<kDppQuadX1, 0xF>(v);
+  v = fmin_step<kDppQuadX2, 0xF>(v);
+  v = fmin_step<kDppHalfMirror, 0xF>(v);
+  v = fmin_step<kDppMirror, 0xF>(v);
+  v = fmin_step<kDppBcast15, 0xA>(v);
+  v = fmin_step<kDppBcast31, 0xC>(v);
+  return __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(v), 63));
+}
+
+// Up to `rounds` rounds of wave-wide argmax over the keys (expert lane+64v
+// holds key[v]). Lane r receives the r-th winner's expert and key; `top` is
+// the first winner's key. Returns the number of winners.
+template <int NV>
+__device__ __forceinline__ int wave_rank(uint32_t (&key)[NV], int rounds, int lane, int &my_e,
+                                         uint32_t &my_key, uint32_t &top) {
+  int n = 0;
+  for (int r = 0; r < rounds; ++r) {
+    uint32_t best = key[0];
+#pragma unroll
+    for (int v = 1; v < NV; ++v) best = key[v] > best ? key[v] : best;
+    best = wave_max_u32(best);
+    if (best == 0) break;
+    int e = 0;
+#pragma unroll
+    for (int v = NV - 1; v >= 0; --v) {  // the lowest index holding `best` wins
+      const unsigned long long b = __ballot(key[v] == best);
+      if (b) e = 64 * v + __builtin_ctzll(b);
+    }
+    if (lane == r) {
+      my_e = e;
+      my_key = best;
+    }
+    if (r == 0) top = best;
+#pragma unroll
+    for (int v = 0; v < NV; ++v)
+      if (lane + 64 * v == e) key[v] = 0;
+    ++n;
+  }
+  return n;
+}
+
+__device__ __forceinline__ bool bit_of(const uint32_t *mask, int e) { return (mask[e >> 5] >> (e & 31)) & 1u; }
+
+// The whole selection, run by one workgroup of kThreads threads. The logits
+// are read with device-scope loads, so they may come from other workgroups
+// of the same kernel. TPW token slots per wave (B <= 16 * TPW): the per-token
+// phases are unrolled over the slots, so a small TPW keeps the code small.
+template <int NV, int TPW>
+__device__ __forceinline__ void select_block(
+    const float *__restrict__ logits, int B, int E, int kind, int k, int k0, int m,
+    int32_t *__restrict__ topk_ids, float *__restrict__ topk_w, int32_t *__restrict__ n_active,
+    int32_t *__restrict__ active_experts, int32_t *__restrict__ expert_offsets,
+    int32_t *__restrict__ pair_token, int32_t *__restrict__ pair_slot,
+    float *__restrict__ batch_mass) {
+  __shared__ uint32_t allowed[kWords];
+  __shared__ uint32_t etok[kMaxE][kTokWords];  // bit t of etok[e]: token t routes to e
+  __shared__ int16_t sel_id[kMaxB][kMaxK];
+  __shared__ float sel_w[kMaxB][kMaxK];
+  __shared__ float psum[kWaves][kMaxE];
+  __shared__ float mass[kMaxE];
+  __shared__ int acnt[kMaxE];
+  __shared__ int apos[kMaxE];
+  __shared__ int aoff[kMaxE];
+  __shared__ int s_n, s_total;
+  __shared__ float tok_mx[kMaxB], tok_sm[kMaxB], tok_thr[kMaxB];  // GREEDY per-token state
+  __shared__ int tok_cnt[kMaxB];
+  __shared__ uint32_t w_best[kWaves];
+  __shared__ int w_e[kWaves];
+  __shared__ int s_pick;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+
+  for (int i = tid; i < kWords; i += kThreads) {
+    uint32_t full = 0;
+    if (kind == MOE_POLICY_TOPK) {
+      const int lo = i * 32;
+      const int nb = min(32, max(0, E - lo));
+      full = nb == 32 ? 0xFFFFFFFFu : ((1u << nb) - 1u);
+    }
+    allowed[i] = full;
+  }
+  for (int i = tid; i < kMaxE * kTokWords; i += kThreads) etok[i / kTokWords][i % kTokWords] = 0;
+
+  // Phase 1: logits into registers. Addresses are clamped so that every load
+  // is in bounds; values outside [B, E) are never used as candidates.
+  float L[TPW][NV];
+#pragma unroll
+  for (int ti = 0; ti < TPW; ++ti) {
+    if (ti * kWaves < B) {  // wave-uniform
+      const int t = min(wave + kWaves * ti, B - 1);
+#pragma unroll
+      for (int v = 0; v < NV; ++v)
+        L[ti][v] = __hip_atomic_load(const_cast<float *>(logits) + t * E + min(lane + 64 * v, E - 1),
+                                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+  __syncthreads();
+
+  // Phase 2: the policy's batch step.
+  if (kind == MOE_POLICY_OEA) {
+#pragma unroll
+    for (int ti = 0; ti < TPW; ++ti) {
+      const int t = wave + kWaves * ti;
+      if (t < B) {
+        uint32_t key[NV];
+#pragma unroll
+        for (int v = 0; v < NV; ++v) key[v] = (lane + 64 * v < E) ? ord_bits(L[ti][v]) : 0u;
+        int e = 0;
+        uint32_t kv = 0, top = 0;
+        const int n = wave_rank<NV>(key, k0, lane, e, kv, top);
+        if (lane < n) atomicOr(&allowed[e >> 5], 1u << (e & 31));
+      }
+    }
+  } else if (kind == MOE_POLICY_BUDGET) {
+    // Per-token softmax over all E experts, then column sums over the batch
+    // in a fixed order (token slot ti outer, wave inner).
+    float macc = 0.0f;  // thread tid < E accumulates expert tid
+    const int rounds = (B + kWaves - 1) / kWaves;
+#pragma unroll
+    for (int ti = 0; ti < TPW; ++ti) {
+      if (ti < rounds) {  // block-uniform: every wave reaches the same barriers
+        const int t = wave + kWaves * ti;
+        float mx = -INFINITY;
+#pragma unroll
+        for (int v = 0; v < NV; ++v)
+          if (lane + 64 * v < E) mx = fmaxf(mx, L[ti][v]);
+        mx = wave_maxf(mx);
+        float sm = 0.0f;
+#pragma unroll
+        for (int v = 0; v < NV; ++v)
+          if (lane + 64 * v < E) sm += expf(L[ti][v] - mx);
+        sm = wave_sum(sm);
+#pragma unroll
+        for (int v = 0; v < NV; ++v) {
+          const int e = lane + 64 * v;
+          if (e < E) psum[wave][e] = (t < B) ? expf(L[ti][v] - mx) / sm : 0.0f;
+        }
+        __syncthreads();
+        if (tid < E) {
+          for (int w = 0; w < kWaves; ++w) macc += psum[w][tid];
+        }
+        __syncthreads();
+      }
+    }
+    if (tid < E) mass[tid] = macc;
+    __syncthreads();
+    if (tid < E) {
+      int rank = 0;
+      for (int e2 = 0; e2 < E; ++e2) {
+        const float o = mass[e2];
+        rank += (o > macc) || (o == macc && e2 < tid);
+      }
+      if (rank < m) atomicOr(&allowed[tid >> 5], 1u << (tid & 31));
+    }
+  } else if (kind == MOE_POLICY_GREEDY) {
+    // Per-token softmax normalisers (probabilities are recomputed from the
+    // logits whenever needed, always by the same expression).
+#pragma unroll
+    for (int ti = 0; ti < TPW; ++ti) {
+      const int t = wave + kWaves * ti;
+      if (t < B) {
+        float mx = -INFINITY;
+#pragma unroll
+        for (int v = 0; v < NV; ++v)
+          if (lane + 64 * v < E) mx = fmaxf(mx, L[ti][v]);
+        mx = wave_maxf(mx);
+        float sm = 0.0f;
+#pragma unroll
+        for (int v = 0; v < NV; ++v)
+          if (lane + 64 * v < E) sm += expf(L[ti][v] - mx);
+        sm = wave_sum(sm);
+        if (lane == 0) {
+          tok_mx[t] = mx;
+          tok_sm[t] = sm;
+          tok_thr[t] = 0.0f;
+          tok_cnt[t] = 0;
+        }
+      }
+    }
+    uint64_t kept = 0;  // bit ti*NV+v: expert lane+64v is among token slot ti's k largest in S
+    __syncthreads();
+    for (int r = 0; r < m; ++r) {
+      // Gains over this wave's tokens, then over the waves in order.
+      float g[NV];
+#pragma unroll
+      for (int v = 0; v < NV; ++v) g[v] = 0.0f;
+#pragma unroll
+      for (int ti = 0; ti < TPW; ++ti) {
+        const int t = wave + kWaves * ti;
+        if (t < B) {
+          const float mx = tok_mx[t], sm = tok_sm[t], thr = tok_thr[t];
+#pragma unroll
+          for (int v = 0; v < NV; ++v) g[v] += fmaxf(0.0f, expf(L[ti][v] - mx) / sm - thr);
+        }
+      }
+#pragma unroll
+      for (int v = 0; v < NV; ++v) {
+        const int e = lane + 64 * v;
+        if (e < E) psum[wave][e] = g[v];
+      }
+      __syncthreads();
+      if (wave * 64 < E) {
+        uint32_t key = 0;  // 0: not a candidate
+        if (tid < E && !bit_of(allowed, tid)) {
+          float gain = 0.0f;
+          for (int w = 0; w < kWaves; ++w) gain += psum[w][tid];
+          key = ord_bits(gain);
+        }
+        const uint32_t best = wave_max_u32(key);
+        const unsigned long long b = __ballot(key == best && key != 0);
+        if (lane == 0) {
+          w_best[wave] = best;
+          w_e[wave] = b ? wave * 64 + __builtin_ctzll(b) : -1;
+        }
+      }
+      __syncthreads();
+      if (tid == 0) {
+        uint32_t best = 0;
+        int e = -1;
+        for (int w = 0; w * 64 < E; ++w)
+          if (w_e[w] >= 0 && w_best[w] > best) {
+            best = w_best[w];
+            e = w_e[w];
+          }
+        s_pick = e;
+        if (e >= 0) allowed[e >> 5] |= 1u << (e & 31);
+      }
+      __syncthreads();
+      const int e = s_pick;
+      if (e < 0) break;  // block-uniform: no expert left
+      // Token slots update their k largest probabilities inside S.
+      const int ve = e >> 6, le = e & 63;
+#pragma unroll
+      for (int ti = 0; ti < TPW; ++ti) {
+        const int t = wave + kWaves * ti;
+        if (t < B) {
+          const float mx = tok_mx[t], sm = tok_sm[t];
+          float pv[NV];
+#pragma unroll
+          for (int v = 0; v < NV; ++v) pv[v] = expf(L[ti][v] - mx) / sm;
+          float pe_l = 0.0f;
+#pragma unroll
+          for (int v = 0; v < NV; ++v)
+            if (v == ve) pe_l = pv[v];
+          const float pe = __shfl(pe_l, le);
+          int cnt = tok_cnt[t];
+          float thr = tok_thr[t];
+          bool changed = false;
+          if (cnt < k) {
+            if (lane == le) kept |= 1ull << (ti * NV + ve);
+            ++cnt;
+            changed = cnt == k;
+          } else if (pe > thr) {
+            // Drop one kept expert holding the threshold (the lowest index).
+            int drop = -1;
+#pragma unroll
+            for (int v = NV - 1; v >= 0; --v) {
+              const unsigned long long b =
+                  __ballot(((kept >> (ti * NV + v)) & 1ull) && pv[v] == thr);
+              if (b) drop = 64 * v + __builtin_ctzll(b);
+            }
+            if (lane == (drop & 63)) kept &= ~(1ull << (ti * NV + (drop >> 6)));
+            if (lane == le) kept |= 1ull << (ti * NV + ve);
+            changed = true;
+          }
+          if (changed) {
+            float mn = INFINITY;
+#pragma unroll
+            for (int v = 0; v < NV; ++v)
+              if ((kept >> (ti * NV + v)) & 1ull) mn = fminf(mn, pv[v]);
+            thr = wave_minf(mn);
+          }
+          if (lane == 0) {
+            tok_cnt[t] = cnt;
+            tok_thr[t] = thr;
+          }
+        }
+      }
+    }
+  }
+  __syncthreads();
+
+  // Phase 3: each token takes its best experts inside the allowed set.
+#pragma unroll
+  for (int ti = 0; ti < TPW; ++ti) {
+    const int t = wave + kWaves * ti;
+    if (t < B) {
+      uint32_t key[NV];
+#pragma unroll
+      for (int v = 0; v < NV; ++v) {
+        const int e = lane + 64 * v;
+        key[v] = (e < E && bit_of(allowed, e)) ? ord_bits(L[ti][v]) : 0u;
+      }
+      int e = 0;
+      uint32_t kv = 0, top = 0;
+      const int n = wave_rank<NV>(key, k, lane, e, kv, top);
+      const float ex = lane < n ? expf(from_ord_bits(kv) - from_ord_bits(top)) : 0.0f;
+      const float tot = wave_sum(ex);
+      if (lane < k) {
+        sel_id[t][lane] = int16_t(lane < n ? e : -1);
+        sel_w[t][lane] = lane < n ? ex / tot : 0.0f;
+      }
+      if (lane < n) atomicOr(&etok[e][t >> 5], 1u << (t & 31));
+    }
+  }
+  __syncthreads();
+
+  // Phase 4: wave 0 counts each expert's tokens and scans the counts; lane l
+  // owns experts l*NV .. l*NV+NV-1 so that the scan runs in expert order.
+  if (wave == 0) {
+    const int nw = (B + 31) >> 5;
+    int c[NV], a[NV];
+    int lc = 0, la = 0;
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
+      const int e = lane * NV + v;
+      int cv = 0;
+      if (e < E)
+        for (int w = 0; w < nw; ++w) cv += __popc(etok[e][w]);
+      c[v] = cv;
+      a[v] = cv > 0;
+      lc += c[v];
+      la += a[v];
+    }
+    int ic = lc, ia = la;  // inclusive scans over lanes
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int oc = __shfl_up(ic, off);
+      const int oa = __shfl_up(ia, off);
+      if (lane >= off) {
+        ic += oc;
+        ia += oa;
+      }
+    }
+    int pc = ic - lc, pa = ia - la;
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
+      const int e = lane * NV + v;
+      if (e < E) {
+        acnt[e] = c[v];
+        aoff[e] = pc;
+        apos[e] = pa;
+      }
+      pc += c[v];
+      pa += a[v];
+    }
+    if (lane == 63) {
+      s_total = ic;
+      s_n = ia;
+    }
+  }
+  __syncthreads();
+
+  // Phase 5: every output, written once, by all threads.
+  const int nact = s_n, total = s_total, P = B * k;
+  if (tid < E && acnt[tid] > 0) {
+    active_experts[apos[tid]] = tid;
+    expert_offsets[apos[tid]] = aoff[tid];
+  }
+  if (tid < E && batch_mass) batch_mass[tid] = mass[tid];
+  for (int i = nact + tid; i < E; i += kThreads) active_experts[i] = -1;
+  for (int i = nact + tid; i <= E; i += kThreads) expert_offsets[i] = total;
+  for (int i = tid; i < P; i += kThreads) {
+    const int t = i / k, j = i - t * k;
+    const int e = sel_id[t][j];
+    topk_ids[i] = e;
+    topk_w[i] = sel_w[t][j];
+    if (e >= 0) {
+      const uint32_t *row = etok[e];
+      int pos = aoff[e];
+      for (int w = 0; w < (t >> 5); ++w) pos += __popc(row[w]);
+      pos += __popc(row[t >> 5] & ((1u << (t & 31)) - 1u));
+      pair_token[pos] = t;
+      pair_slot[pos] = j;
+    }
+  }
+  for (int i = total + tid; i < P; i += kThreads) {
+    pair_token[i] = -1;
+    pair_slot[i] = -1;
+  }
+  if (tid == 0) n_active[0] = nact;
+}
+
+// Calls f(NV tag, TPW tag) with the compile-time expert and token-slot
+// counts that cover E and B.
+template <typename F>
+__host__ void dispatch_select_shape(int B, int E, F &&f) {
+  auto by_b = [&](auto nv) {
+    if (B <= kWaves) f(nv, std::integral_constant<int, 1>{});
+    else if (B <= 4 * kWaves) f(nv, std::integral_constant<int, 4>{});
+    else f(nv, std::integral_constant<int, kMaxTokPerWave>{});
+  };
+  if (E <= 64) by_b(std::integral_constant<int, 1>{});
+  else if (E <= 128) by_b(std::integral_constant<int, 2>{});
+  else by_b(std::integral_constant<int, 4>{});
+}
+
+}  // namespace
+}  // namespace moe

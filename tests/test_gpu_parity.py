@@ -63,6 +63,7 @@ def _assert_sync_words_clear(ws):
     words = ws[:2048].view(torch.int32).cpu().numpy()
     assert words[0] == 0, f"barrier count left at {words[0]}"
     assert words[64] == 0, "a grid-barrier wait exceeded its bound"
+    assert words[96] == 0, "the router + selection counter was left non-zero"
     assert not words[128:384].any(), "a router tile counter was left non-zero"
 
 
