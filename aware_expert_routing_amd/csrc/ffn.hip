@@ -51,14 +51,19 @@ constexpr int kLdsBytes = 160 * 1024;
 static_assert(kStripCols == 64 && kBK == 128, "tile constants");
 
 // Routing lists staged in LDS once per workgroup (the loop reads them with
-// the inline-assembly helpers below).
-constexpr int kMetaTok = 0;                            // uint8 token of each pair
-constexpr int kMetaRow = kMetaTok + kMaxPairs;         // int16 token slot t*k+j of each pair
-constexpr int kMetaAct = kMetaRow + 2 * kMaxPairs;     // int16 active expert list
-constexpr int kMetaOff = kMetaAct + 2 * kMaxE;         // int16 CSR offsets
-constexpr int kMetaLast = kMetaOff + 2 * (kMaxE + 1);  // int32 tokens whose strip this pass completes
-constexpr int kMetaNLast = kMetaLast + 4 * kMaxTok;    // int32 their number
-constexpr int kMetaBytes = kMetaNLast + 16;
+// the inline-assembly helpers below). Every field is aligned to its element
+// size (LDS atomics need natural alignment) and the area to 16 bytes.
+constexpr int kMetaLast = 0;                            // int32 tokens whose strip this pass completes
+constexpr int kMetaNLast = kMetaLast + 4 * kMaxTok;     // int32 their number
+constexpr int kMetaFill = kMetaNLast + 16;              // uint32 filled slots of each token
+constexpr int kMetaRow = kMetaFill + 4 * kMaxB;         // int16 token slot t*k+j of each pair
+constexpr int kMetaAct = kMetaRow + 2 * kMaxPairs;      // int16 active expert list
+constexpr int kMetaOff = kMetaAct + 2 * kMaxE;          // int16 CSR offsets
+constexpr int kMetaTok = kMetaOff + 2 * (kMaxE + 1);    // uint8 token of each pair
+constexpr int kMetaBytes = (kMetaTok + kMaxPairs + 15) / 16 * 16;
+static_assert(kMetaNLast % 4 == 0 && kMetaFill % 4 == 0 && kMetaRow % 2 == 0 && kMetaAct % 2 == 0 &&
+                  kMetaOff % 2 == 0,
+              "meta field alignment");
 
 // LDS plan of one instantiation. A stage slot holds NMAT weight tiles
 // [kBK rows][64 columns] and the A tile, stored per k-step as
@@ -220,38 +225,39 @@ __device__ __forceinline__ void lds_b128<4>(const uint32_t (&a)[4], bf16x8_t (&x
                : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]));
 }
 
-// Grid-barrier words in the workspace: arrival count, generation, error flag
-// (each on its own 128-byte line). The count is back at zero after every
-// barrier; the generation only grows.
+// Grid-barrier words in the workspace, each on its own 128-byte line: the
+// arrival count (counts every arrival of the launch, zero at launch start and
+// end), the release word (the index of the last barrier completed) and the
+// error flag. Arrivals and polls touch different lines, so polling does not
+// slow the arrivals' atomics.
 constexpr int kSyncCount = 0;
-constexpr int kSyncGen = 32;
+constexpr int kSyncRelease = 32;
 constexpr int kSyncErr = 64;
 constexpr uint32_t kSpinLimit = 1u << 20;
 
-// All workgroups of the grid (resident together: one per CU at most) meet
-// here; one wave of each workgroup takes part (its lanes wait for lane 0).
-// Every store that another workgroup reads after the barrier is a
-// device-scope store made before the arrival by a wave whose stores have
-// completed (s_waitcnt vmcnt(0)), and those reads are device-scope loads, so
-// no cache maintenance is needed. A wait that does not end within
-// kSpinLimit polls sets the error word and returns, so the kernel always
-// terminates.
-__device__ __forceinline__ void grid_barrier_wave(uint32_t *sync) {
+// Barrier `index` (1, 2, ... within a launch) of all workgroups of the grid
+// (resident together: one per CU at most); one wave of each workgroup takes
+// part (its lanes wait for lane 0). An arrival is one atomic add whose old
+// value tells whether it completes the barrier; the last arriver stores the
+// index into the release word, the others poll that word. The final barrier's
+// last arriver puts the count back to zero for the next launch (nothing else
+// touches it in this launch). Every store that another workgroup reads after
+// the barrier is a device-scope store made before the arrival by a wave whose
+// stores have completed (s_waitcnt vmcnt(0)), and those reads are
+// device-scope loads, so no cache maintenance is needed. A wait that does not
+// end within kSpinLimit polls sets the error word and returns, so the kernel
+// always terminates.
+__device__ __forceinline__ void grid_barrier_wave(uint32_t *sync, uint32_t index, bool final_barrier) {
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   if ((threadIdx.x & 63) == 0) {
-    uint32_t *count = sync + kSyncCount, *gen = sync + kSyncGen;
-    const uint32_t g0 = __hip_atomic_load(gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    // The generation must be read before this workgroup's arrival can let
-    // the last arriver advance it.
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    const uint32_t arrived =
-        __hip_atomic_fetch_add(count, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (arrived == gridDim.x - 1) {
-      __hip_atomic_store(count, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      __hip_atomic_fetch_add(gen, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const uint32_t before =
+        __hip_atomic_fetch_add(sync + kSyncCount, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (before == index * gridDim.x - 1) {
+      if (final_barrier) __hip_atomic_store(sync + kSyncCount, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(sync + kSyncRelease, index, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     } else {
-      for (uint32_t n = 0; __hip_atomic_load(gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == g0;
+      for (uint32_t n = 0;
+           __hip_atomic_load(sync + kSyncRelease, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != index;
            ++n) {
         if (n >= kSpinLimit) {
           __hip_atomic_store(sync + kSyncErr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -528,13 +534,14 @@ __device__ __forceinline__ void epilogue(const Cursor &c, const Params &p, uint3
     }
 }
 
-// h = SiLU(g) * u from the slice partial sums, spread over wave 0 of every
-// workgroup. All loads of a lane are issued before the first is used.
-__device__ __forceinline__ void h_phase_wave(const Params &p, int total) {
+// h = SiLU(g) * u from the slice partial sums, spread over waves 0 and 1 of
+// every workgroup (threads 0..127). All loads of a lane are issued before the
+// first is used; the stores have completed when it returns.
+__device__ __forceinline__ void h_phase_waves01(const Params &p, int total) {
   const int q4 = p.I / 4;
   const int n = total * q4;
   const uint32_t blk = uint32_t(p.P) * uint32_t(p.I) * 4u;  // bytes of one [P][I] block
-  for (int idx = blockIdx.x * 64 + (threadIdx.x & 63); idx < n; idx += gridDim.x * 64) {
+  for (int idx = blockIdx.x * 128 + threadIdx.x; idx < n; idx += gridDim.x * 128) {
     const int pr = idx / q4;
     const int c = (idx - pr * q4) * 4;
     const uint32_t off = (uint32_t(pr) * uint32_t(p.I) + uint32_t(c)) * 4u;
@@ -560,6 +567,15 @@ __device__ __forceinline__ void h_phase_wave(const Params &p, int total) {
                        (uint64_t(f32_to_bf16(silu(g.w) * u.w)) << 48);
     st_dev(reinterpret_cast<uint64_t *>(p.h + size_t(pr) * p.I + c), o);
   }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
+// s_barrier without the wait for outstanding memory operations that
+// __syncthreads adds: copies in flight stay in flight.
+__device__ __forceinline__ void barrier_no_wait() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
 }
 
 // End of a down pass (its rows stored by every wave). Each token of the pass
@@ -581,8 +597,7 @@ __device__ __forceinline__ void finish_down(const Cursor &c, const Params &p, un
     int t = 0;
     if (lane < T) {
       t = meta[kMetaTok + pbase + lane];
-      int filled = 0;
-      for (int j = 0; j < p.k; ++j) filled += p.ids[t * p.k + j] >= 0;
+      const int filled = reinterpret_cast<const uint32_t *>(meta + kMetaFill)[t];
       const uint32_t before = __hip_atomic_fetch_add(p.tok_cnt + t * p.n_dstrips + c.strip, 1u,
                                                      __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       mine = before == uint32_t(filled - 1);
@@ -638,11 +653,12 @@ __device__ __forceinline__ void finish_down(const Cursor &c, const Params &p, un
 // The change from gate/up to down in a workgroup: every gate/up stage of it
 // has been consumed and no down stage issued (the producer stops at the first
 // one); `first` is the next stage index. Wave 0 meets the grid at the first
-// barrier (gate/up partial sums complete), forms its share of h and meets the
-// grid again (h complete); meanwhile waves 1-3 copy the weights of the next
-// kD down stages, wave 0's share included, so those copies overlap the
-// barriers without delaying wave 0's waits (vmcnt completes in order). Then
-// every wave copies its h rows of those stages and waits for all of them.
+// barrier (gate/up partial sums complete); waves 0 and 1 then form this
+// workgroup's share of h, and wave 0 meets the grid again (h complete).
+// Meanwhile waves 2 and 3 copy the weights of the next kD down stages, all
+// four shares, so those copies overlap the barriers without delaying the
+// waits of waves 0 and 1 (vmcnt completes in order). Then every wave copies
+// its h rows of those stages and waits for all of them.
 template <int MTX>
 __device__ __forceinline__ void change_to_down(const Params &p, const Stream<MTX> &st, Cursor &prod,
                                                int &issued, int first, unsigned char *stages,
@@ -653,19 +669,21 @@ __device__ __forceinline__ void change_to_down(const Params &p, const Stream<MTX
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's gate/up stores
   __syncthreads();
   if (st.wave == 0) {
-    grid_barrier_wave(p.sync);
-    h_phase_wave(p, total);
-    grid_barrier_wave(p.sync);
-  } else {
+    grid_barrier_wave(p.sync, 1, false);
+  } else if (st.wave >= 2) {
     Cursor q = prod;
     for (int n = 0; n < kD && q.valid; ++n) {
       unsigned char *slot = stages + ((first + n) % kS) * S::kSlot;
-      if (st.wave == 1) st.issue_dn_weights_as(q, slot, 0);
+      st.issue_dn_weights_as(q, slot, st.wave - 2);
       st.issue_dn_weights_as(q, slot, st.wave);
       st.advance(q);
     }
   }
-  __syncthreads();
+  barrier_no_wait();
+  if (st.wave < 2) h_phase_waves01(p, total);
+  barrier_no_wait();
+  if (st.wave == 0) grid_barrier_wave(p.sync, 2, true);
+  barrier_no_wait();
   for (int n = 0; n < kD && prod.valid; ++n) {
     st.issue_a(prod, stages + ((first + n) % kS) * S::kSlot);
     st.advance(prod);
@@ -708,8 +726,13 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_kernel(Params p,
     meta[kMetaTok + i] = uint8_t(t);
     reinterpret_cast<int16_t *>(meta + kMetaRow)[i] = int16_t(t * p.k + p.pair_slot[i]);
   }
+  uint32_t *fill = reinterpret_cast<uint32_t *>(meta + kMetaFill);
+  for (int t = threadIdx.x; t < p.B; t += kThreads) fill[t] = 0;
   __syncthreads();
   const int total = reinterpret_cast<const int16_t *>(meta + kMetaOff)[nact];
+  // Filled slots of each token = its pairs in the list.
+  for (int i = threadIdx.x; i < total; i += kThreads) atomicAdd(fill + meta[kMetaTok + i], 1u);
+  __syncthreads();
 
   const Stream<MTX> st(p, lds_addr(meta));
   Cursor cons;

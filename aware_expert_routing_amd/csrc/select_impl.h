@@ -142,8 +142,8 @@ __device__ __forceinline__ float wave_minf(float v) {
 // holds key[v]). Lane r receives the r-th winner's expert and key; `top` is
 // the first winner's key. Returns the number of winners.
 template <int NV>
-__device__ __forceinline__ int wave_rank(uint32_t (&key)[NV], int rounds, int lane, int &my_e,
-                                         uint32_t &my_key, uint32_t &top) {
+__device__ __forceinline__ int wave_rank(uint32_t (&key)[NV], int rounds, int base, int lane,
+                                         int &my_e, uint32_t &my_key, uint32_t &top) {
   int n = 0;
   for (int r = 0; r < rounds; ++r) {
     uint32_t best = key[0];
@@ -157,11 +157,11 @@ __device__ __forceinline__ int wave_rank(uint32_t (&key)[NV], int rounds, int la
       const unsigned long long b = __ballot(key[v] == best);
       if (b) e = 64 * v + __builtin_ctzll(b);
     }
-    if (lane == r) {
+    if (lane == base + r) {
       my_e = e;
       my_key = best;
     }
-    if (r == 0) top = best;
+    if (base + r == 0) top = best;
 #pragma unroll
     for (int v = 0; v < NV; ++v)
       if (lane + 64 * v == e) key[v] = 0;
@@ -229,7 +229,19 @@ __device__ __forceinline__ void select_block(
   }
   __syncthreads();
 
-  // Phase 2: the policy's batch step.
+  // Phase 2: the policy's batch step. OEA keeps each token's top-k0 picks
+  // (lane j holds pick j): they are also the first k0 picks of phase 3, since
+  // they are the token's largest logits and all of them are allowed.
+  int pick_e[TPW], pick_n[TPW];
+  uint32_t pick_key[TPW], pick_top[TPW], picked[TPW];  // bit v of picked: candidate lane+64v taken
+#pragma unroll
+  for (int ti = 0; ti < TPW; ++ti) {
+    pick_e[ti] = 0;
+    pick_n[ti] = 0;
+    pick_key[ti] = 0;
+    pick_top[ti] = 0;
+    picked[ti] = 0;
+  }
   if (kind == MOE_POLICY_OEA) {
 #pragma unroll
     for (int ti = 0; ti < TPW; ++ti) {
@@ -238,10 +250,14 @@ __device__ __forceinline__ void select_block(
         uint32_t key[NV];
 #pragma unroll
         for (int v = 0; v < NV; ++v) key[v] = (lane + 64 * v < E) ? ord_bits(L[ti][v]) : 0u;
-        int e = 0;
-        uint32_t kv = 0, top = 0;
-        const int n = wave_rank<NV>(key, k0, lane, e, kv, top);
-        if (lane < n) atomicOr(&allowed[e >> 5], 1u << (e & 31));
+        uint32_t cand = 0;
+#pragma unroll
+        for (int v = 0; v < NV; ++v) cand |= uint32_t(key[v] != 0) << v;
+        const int n = wave_rank<NV>(key, k0, 0, lane, pick_e[ti], pick_key[ti], pick_top[ti]);
+#pragma unroll
+        for (int v = 0; v < NV; ++v) picked[ti] |= uint32_t(((cand >> v) & 1u) && key[v] == 0) << v;
+        pick_n[ti] = n;
+        if (lane < n) atomicOr(&allowed[pick_e[ti] >> 5], 1u << (pick_e[ti] & 31));
       }
     }
   } else if (kind == MOE_POLICY_BUDGET) {
@@ -422,11 +438,12 @@ __device__ __forceinline__ void select_block(
 #pragma unroll
       for (int v = 0; v < NV; ++v) {
         const int e = lane + 64 * v;
-        key[v] = (e < E && bit_of(allowed, e)) ? ord_bits(L[ti][v]) : 0u;
+        key[v] = (e < E && bit_of(allowed, e) && !((picked[ti] >> v) & 1u)) ? ord_bits(L[ti][v]) : 0u;
       }
-      int e = 0;
-      uint32_t kv = 0, top = 0;
-      const int n = wave_rank<NV>(key, k, lane, e, kv, top);
+      // Continue after the picks phase 2 already made (none unless OEA).
+      int e = pick_e[ti];
+      uint32_t kv = pick_key[ti], top = pick_top[ti];
+      const int n = pick_n[ti] + wave_rank<NV>(key, k - pick_n[ti], pick_n[ti], lane, e, kv, top);
       const float ex = lane < n ? expf(from_ord_bits(kv) - from_ord_bits(top)) : 0.0f;
       const float tot = wave_sum(ex);
       if (lane < k) {
