@@ -227,7 +227,7 @@ __device__ __forceinline__ void lds_b128<4>(const uint32_t (&a)[4], bf16x8_t (&x
 
 // Grid-barrier words in the workspace, each on its own 128-byte line: the
 // arrival count (counts every arrival of the launch, zero at launch start and
-// end), the release word (the index of the last barrier completed) and the
+// end), the release word (counts completed barriers, never reset) and the
 // error flag. Arrivals and polls touch different lines, so polling does not
 // slow the arrivals' atomics.
 constexpr int kSyncCount = 0;
@@ -235,29 +235,39 @@ constexpr int kSyncRelease = 32;
 constexpr int kSyncErr = 64;
 constexpr uint32_t kSpinLimit = 1u << 20;
 
+// The release word as the launch found it. Every workgroup reads it before
+// its first arrival and no barrier completes before every workgroup has
+// arrived, so all of them read the same value.
+__device__ __forceinline__ uint32_t release_base(const uint32_t *sync) {
+  return __hip_atomic_load(const_cast<uint32_t *>(sync) + kSyncRelease, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // Barrier `index` (1, 2, ... within a launch) of all workgroups of the grid
 // (resident together: one per CU at most); one wave of each workgroup takes
 // part (its lanes wait for lane 0). An arrival is one atomic add whose old
-// value tells whether it completes the barrier; the last arriver stores the
-// index into the release word, the others poll that word. The final barrier's
-// last arriver puts the count back to zero for the next launch (nothing else
-// touches it in this launch). Every store that another workgroup reads after
-// the barrier is a device-scope store made before the arrival by a wave whose
-// stores have completed (s_waitcnt vmcnt(0)), and those reads are
-// device-scope loads, so no cache maintenance is needed. A wait that does not
-// end within kSpinLimit polls sets the error word and returns, so the kernel
-// always terminates.
-__device__ __forceinline__ void grid_barrier_wave(uint32_t *sync, uint32_t index, bool final_barrier) {
+// value tells whether it completes the barrier; the last arriver stores
+// base + index into the release word, the others poll that word. The final
+// barrier's last arriver puts the count back to zero for the next launch
+// (nothing else touches it in this launch). Every store that another
+// workgroup reads after the barrier is a device-scope store made before the
+// arrival by a wave whose stores have completed (s_waitcnt vmcnt(0)), and
+// those reads are device-scope loads, so no cache maintenance is needed. A
+// wait that does not end within kSpinLimit polls sets the error word and
+// returns, so the kernel always terminates.
+__device__ __forceinline__ void grid_barrier_wave(uint32_t *sync, uint32_t base, uint32_t index,
+                                                  bool final_barrier) {
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   if ((threadIdx.x & 63) == 0) {
     const uint32_t before =
         __hip_atomic_fetch_add(sync + kSyncCount, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const uint32_t target = base + index;
     if (before == index * gridDim.x - 1) {
       if (final_barrier) __hip_atomic_store(sync + kSyncCount, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(sync + kSyncRelease, index, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(sync + kSyncRelease, target, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     } else {
       for (uint32_t n = 0;
-           __hip_atomic_load(sync + kSyncRelease, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != index;
+           __hip_atomic_load(sync + kSyncRelease, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != target;
            ++n) {
         if (n >= kSpinLimit) {
           __hip_atomic_store(sync + kSyncErr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -274,7 +284,7 @@ struct Params {
   const uint16_t *x;          // [B, d]
   const uint16_t *W[3];       // G, U: [E, d, I]; D: [E, I, d]
   int B, d, E, I, k;
-  int slices, slice_rows;     // gate/up reduction slices over d
+  int slices, slice_rows;     // gate/up reduction slices over d (1: whole of d, h formed in the epilogue)
   int P;                      // B * k
   float *gpart;               // [slices][2][P][I] gate/up partial sums by pair
   uint16_t *h;                // [P][I] SiLU(g) * u by pair
@@ -507,6 +517,25 @@ __device__ __forceinline__ void epilogue(const Cursor &c, const Params &p, uint3
   const int g = lane >> 4, j = lane & 15;
   const int T = min(kMaxTok, c.T - c.pass * kMaxTok);
   const int pbase = c.p0 + c.pass * kMaxTok;
+  if (c.up && p.slices == 1) {
+    // The whole reduction is in the accumulators: h = SiLU(g) * u by pair.
+    const int col = c.strip * kStripCols + 16 * wave + j;
+    if (col < p.I) {
+      const __amdgpu_buffer_rsrc_t rh = make_rsrc(p.h, uint32_t(p.P) * uint32_t(p.I) * 2u);
+#pragma unroll
+      for (int t4 = 0; t4 < MTX; ++t4)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int m = 16 * t4 + 4 * g + i;
+          if (m < T) {
+            const uint16_t hv = f32_to_bf16(silu(acc.mf[0][t4][i]) * acc.mf[1][t4][i]);
+            __builtin_amdgcn_raw_buffer_store_b16(hv, rh, int((uint32_t(pbase + m) * uint32_t(p.I) + uint32_t(col)) * 2u),
+                                                  0, kPolicyDevice);
+          }
+        }
+    }
+    return;
+  }
   float *dst0, *dst1;
   int col0, col1, ld;
   if (c.up) {
@@ -662,14 +691,16 @@ __device__ __forceinline__ void finish_down(const Cursor &c, const Params &p, un
 template <int MTX>
 __device__ __forceinline__ void change_to_down(const Params &p, const Stream<MTX> &st, Cursor &prod,
                                                int &issued, int first, unsigned char *stages,
-                                               int total) {
+                                               int total, uint32_t rel_base) {
   using S = Shape<2, MTX>;
   constexpr int kS = S::kStages;
   constexpr int kD = kS - 1;
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's gate/up stores
   __syncthreads();
+  const bool sliced = p.slices > 1;  // else the gate/up epilogues formed h
   if (st.wave == 0) {
-    grid_barrier_wave(p.sync, 1, false);
+    if (sliced) grid_barrier_wave(p.sync, rel_base, 1, false);
+    else grid_barrier_wave(p.sync, rel_base, 1, true);
   } else if (st.wave >= 2) {
     Cursor q = prod;
     for (int n = 0; n < kD && q.valid; ++n) {
@@ -680,10 +711,12 @@ __device__ __forceinline__ void change_to_down(const Params &p, const Stream<MTX
     }
   }
   barrier_no_wait();
-  if (st.wave < 2) h_phase_waves01(p, total);
-  barrier_no_wait();
-  if (st.wave == 0) grid_barrier_wave(p.sync, 2, true);
-  barrier_no_wait();
+  if (sliced) {
+    if (st.wave < 2) h_phase_waves01(p, total);
+    barrier_no_wait();
+    if (st.wave == 0) grid_barrier_wave(p.sync, rel_base, 2, true);
+    barrier_no_wait();
+  }
   for (int n = 0; n < kD && prod.valid; ++n) {
     st.issue_a(prod, stages + ((first + n) % kS) * S::kSlot);
     st.advance(prod);
@@ -715,7 +748,8 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_kernel(Params p,
   unsigned char *meta = lds + kS * S::kSlot;
 
   // Routing lists into LDS, in one round of independent loads (entries past
-  // the active ones are never read).
+  // the active ones are never read), and the barrier release base.
+  const uint32_t rel_base = release_base(p.sync);
   const int nact = n_active[0];
   for (int i = threadIdx.x; i <= p.E; i += kThreads) {
     reinterpret_cast<int16_t *>(meta + kMetaOff)[i] = int16_t(offsets[i]);
@@ -733,6 +767,17 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_kernel(Params p,
   // Filled slots of each token = its pairs in the list.
   for (int i = threadIdx.x; i < total; i += kThreads) atomicAdd(fill + meta[kMetaTok + i], 1u);
   __syncthreads();
+
+  // Whole-d gate/up tiles when the active experts' tiles (expert x 64-column
+  // strip of I) fill enough of the grid to keep HBM busy: each tile then
+  // forms its h columns itself and the grid meets once. Otherwise the d
+  // slices spread the gate/up work over the grid and h is formed from
+  // their partial sums between two grid barriers.
+  const int up_tiles = nact * ((p.I + kStripCols - 1) / kStripCols);
+  if (5 * up_tiles >= 3 * int(gridDim.x)) {
+    p.slices = 1;
+    p.slice_rows = p.d;
+  }
 
   const Stream<MTX> st(p, lds_addr(meta));
   Cursor cons;
@@ -760,7 +805,7 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_kernel(Params p,
   bool h_ready = false;
   for (int s = 0; cons.valid; ++s) {
     if (!cons.up && !h_ready) {
-      change_to_down<MTX>(p, st, prod, issued, s, stages, total);
+      change_to_down<MTX>(p, st, prod, issued, s, stages, total, rel_base);
       h_ready = true;
     }
     // Stage s must have landed; the stages issued after it may stay in flight
@@ -786,7 +831,7 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_kernel(Params p,
     }
     st.advance(cons);
   }
-  if (!h_ready) change_to_down<MTX>(p, st, prod, issued, 0, stages, total);  // no down items here
+  if (!h_ready) change_to_down<MTX>(p, st, prod, issued, 0, stages, total, rel_base);  // no down items here
 }
 
 // ------------------------------------------------------------- combine (f32)
