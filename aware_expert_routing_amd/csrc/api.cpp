@@ -62,7 +62,7 @@ moe_status_t check_workspace(const void *ws, size_t have, size_t need) {
 // entry point.
 size_t route_bytes(int B, int d, int E) {
   const size_t tiles = size_t(ceil_div(E, kRouterTile)) * ceil_div(B, kRouterTile);
-  return router_offset(B, d) +
+  return kCounterBytes +
          align256(tiles * ceil_div(d, kRouterRows) * kRouterTile * kRouterTile * sizeof(float));
 }
 
@@ -95,7 +95,7 @@ moe_status_t moe_route(const void *x, const void *w_g, const float *bias, moe_dt
   MOE_TRY(check_workspace(workspace, workspace_bytes, route_bytes(B, d, E)));
   hipStream_t s = static_cast<hipStream_t>(stream);
   char *ws = static_cast<char *>(workspace);
-  float *part = reinterpret_cast<float *>(ws + router_offset(B, d));
+  float *part = reinterpret_cast<float *>(ws + kCounterBytes);
   uint32_t *cnt = reinterpret_cast<uint32_t *>(ws + kRouterCntOffset);
   return hip_status(launch_router(x, w_g, bias, dt, B, d, E, part, cnt, logits, s));
 }
@@ -152,11 +152,11 @@ moe_status_t moe_layer_decode(const void *x, const void *w_g, const float *bias,
   hipStream_t s = static_cast<hipStream_t>(stream);
   char *ws = static_cast<char *>(workspace);
   if (dt == MOE_BF16) {
-    uint32_t *cnt = reinterpret_cast<uint32_t *>(ws + plan.sync + kRouteSelectCntOffset);
+    uint32_t *cnt = reinterpret_cast<uint32_t *>(ws + kRouteSelectCntOffset);
     MOE_TRY(hip_status(launch_route_select(x, w_g, bias, B, d, E, logits, cnt, policy, *routing, s)));
   } else {
     float *part = reinterpret_cast<float *>(ws + plan.router_part);
-    uint32_t *cnt = reinterpret_cast<uint32_t *>(ws + plan.sync + kRouterCntOffset);
+    uint32_t *cnt = reinterpret_cast<uint32_t *>(ws + kRouterCntOffset);
     MOE_TRY(hip_status(launch_router(x, w_g, bias, dt, B, d, E, part, cnt, logits, s)));
     MOE_TRY(hip_status(launch_select(logits, B, E, policy, *routing, s)));
   }

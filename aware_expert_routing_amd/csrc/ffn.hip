@@ -987,8 +987,8 @@ hipError_t launch_expert_ffn(const void *x, const void *w_gate, const void *w_up
     p.w = r.topk_w;
     p.pair_token = r.pair_token;
     p.pair_slot = r.pair_slot;
-    p.sync = reinterpret_cast<uint32_t *>(ws + plan.sync);
-    p.tok_cnt = reinterpret_cast<uint32_t *>(ws + plan.tok_cnt);
+    p.sync = reinterpret_cast<uint32_t *>(ws);
+    p.tok_cnt = reinterpret_cast<uint32_t *>(ws + kTokCntOffset);
     p.n_dstrips = ceil_div(d, 2 * kStripCols);
     // One workgroup per CU at most, so that the whole grid is resident and
     // the grid barriers cannot wait on a workgroup that has not started.

@@ -29,10 +29,23 @@ constexpr int kStageRows = 128;     // weight rows staged in LDS per pipeline st
 
 inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
+inline size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
+
+// The first kCounterBytes of every workspace hold counters at fixed offsets
+// (the same for every size of call, so that calls of different sizes may
+// share a workspace): the expert FFN's grid-barrier words (first 384 bytes),
+// the fused router + selection counter, the router's per-tile counters (up
+// to 256 tiles) and the FFN's per-(token, 128-column strip) counters. All are
+// zero before the workspace's first use. Every call leaves the counters at
+// zero; the barrier's release word only grows. No other step writes them.
+constexpr size_t kSyncBytes = 2048;
+constexpr size_t kRouteSelectCntOffset = 384;  // fused router + selection: tiles done
+constexpr size_t kRouterCntOffset = 512;
+constexpr size_t kTokCntOffset = kSyncBytes;  // uint32 [kMaxB][kMaxDim / 128]
+constexpr size_t kCounterBytes = kTokCntOffset + size_t(kMaxB) * (kMaxDim / (2 * kStripCols)) * 4;
+
 // Workspace carve-up. Every segment starts on a 256-byte boundary.
 struct Workspace {
-  size_t sync;         // uint32 grid-barrier words of the expert FFN (kSyncBytes)
-  size_t tok_cnt;      // uint32 [B][ceil(d/128)] per-(token, strip) counters of the expert FFN
   size_t router_part;  // float [tiles][router_slices][16 x 16] partial logit tiles
   size_t up_part;      // float [up_slices][2][B*k][I]   (gate, up partial sums)
   size_t h;            // bf16 or float [B*k][I]
@@ -43,23 +56,6 @@ struct Workspace {
   int up_slices;
   int up_slice_rows;
 };
-
-inline size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
-
-// Bytes at the start of the workspace that hold synchronisation words: the
-// expert FFN's grid-barrier words (first 512 bytes), then the router's
-// per-tile counters (up to 256 tiles); the FFN's per-token counters follow.
-// All must be zero before the workspace's first use; every call leaves them
-// ready for the next one. No other step writes them.
-constexpr size_t kSyncBytes = 2048;
-constexpr size_t kRouteSelectCntOffset = 384;  // fused router + selection: tiles done
-constexpr size_t kRouterCntOffset = 512;
-
-// Offset of the router's partial sums: after the expert FFN's synchronisation
-// words (barrier words, then per-token counters), which depend on B and d only.
-inline size_t router_offset(int B, int d) {
-  return kSyncBytes + align256(size_t(B) * ceil_div(d, 2 * kStripCols) * sizeof(uint32_t));
-}
 
 inline Workspace plan_workspace(int B, int d, int E, int I, int k, moe_dtype_t dt) {
   Workspace w{};
@@ -73,14 +69,11 @@ inline Workspace plan_workspace(int B, int d, int E, int I, int k, moe_dtype_t d
   w.up_slice_rows = rows;
   const size_t P = size_t(B) * size_t(k);
   const size_t esz = (dt == MOE_BF16) ? 2 : 4;
-  size_t off = 0;
-  w.sync = off;
-  w.tok_cnt = off + kSyncBytes;
-  off = router_offset(B, d);
+  size_t off = kCounterBytes;
   w.router_part = off;
   off = align256(off + router_tiles * w.router_slices * kRouterTile * kRouterTile * sizeof(float));
   w.up_part = off;
-  off = align256(off + size_t(w.up_slices) * 2 * P * I * sizeof(float));
+  if (dt == MOE_BF16) off = align256(off + size_t(w.up_slices) * 2 * P * I * sizeof(float));
   w.h = off;
   off = align256(off + P * I * esz);
   w.down_part = off;

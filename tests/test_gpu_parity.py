@@ -56,15 +56,23 @@ def _run_layer(cfg: LayerConfig, inp, dev, B: int, policy: str, k0: int, m: int,
     return lg.t.cpu().numpy(), routing_numpy(r), y.t
 
 
+# Fixed counter region at the start of every workspace (byte offsets): barrier
+# count (0), release word (128), error word (256), router + selection counter
+# (384), router tile counters (512..1535), per-(token, strip) counters
+# (2048 + 4 * 256 * 128 bytes).
+_TOK_CNT = (2048, 2048 + 4 * 256 * 128)
+
+
 def _assert_sync_words_clear(ws):
     """The FFN's grid-barrier count returns to zero, its error word stays
-    zero (a barrier wait never ran out) and the router's tile counters are
-    back at zero."""
-    words = ws[:2048].view(torch.int32).cpu().numpy()
+    zero (no bounded wait ran out), and every counter (router + selection,
+    router tiles, per-token strips) is back at zero."""
+    words = ws[:_TOK_CNT[1]].view(torch.int32).cpu().numpy()
     assert words[0] == 0, f"barrier count left at {words[0]}"
-    assert words[64] == 0, "a grid-barrier wait exceeded its bound"
+    assert words[64] == 0, "a bounded wait exceeded its limit"
     assert words[96] == 0, "the router + selection counter was left non-zero"
     assert not words[128:384].any(), "a router tile counter was left non-zero"
+    assert not words[_TOK_CNT[0] // 4:_TOK_CNT[1] // 4].any(), "a per-token counter was left non-zero"
 
 
 def _oracle(cfg, inp, B, policy, k0, m, tokens=None):
@@ -161,6 +169,27 @@ def test_workspace_reused_across_calls():
     # Fresh workspace, same call: same bits.
     _, _, y_fresh = _run_layer(cfg, inp, dev, B, "oea", 1, 0)
     assert torch.equal(outs[4], y_fresh)
+
+
+def test_workspace_shared_across_sizes():
+    """One workspace (sized for the largest call) serves calls of different
+    batch sizes in a row: each output equals a fresh workspace's, bit for bit."""
+    cfg = CONFIGS["qwen3_30b_bf16"]
+    inp, dev = _layer_inputs("qwen3_30b_bf16")
+    Bmax = max(cfg.batches)
+    ws = L.alloc_workspace(Bmax, cfg.d, cfg.E, cfg.I, cfg.k, torch.bfloat16)
+    for B, pol, p in ((Bmax, "topk", 0), (1, "oea", 2), (16, "oea", 4), (4, "topk", 0), (Bmax, "oea", 3)):
+        a = policy_args(pol, p)
+        x = dev["x"][:B].contiguous()
+        r = L.Routing(B, cfg.E, cfg.k)
+        lg = torch.empty((B, cfg.E), dtype=torch.float32, device="cuda")
+        y = torch.empty((B, cfg.d), dtype=torch.bfloat16, device="cuda")
+        L.moe_layer_decode(x, dev["w_g"], dev["bias"], dev["w_gate"], dev["w_up"], dev["w_down"],
+                           L.make_policy(a["policy"], cfg.k, a["k0"], a["m"]), lg, r, y, ws)
+        torch.cuda.synchronize()
+        _assert_sync_words_clear(ws)
+        _, _, y_fresh = _run_layer(cfg, inp, dev, B, pol, a["k0"], a["m"])
+        assert torch.equal(y, y_fresh), f"B={B} {pol}{p}"
 
 
 def test_route_select_ffn_equal_layer():
