@@ -29,7 +29,7 @@ MOE_POLICY_BUDGET = 2
 MOE_POLICY_GREEDY = 3
 
 EXPORTS = ("moe_workspace_bytes", "moe_route", "moe_select", "moe_expert_ffn",
-           "moe_layer_decode", "moe_status_string")
+           "moe_layer_decode", "moe_status_string", "moe_read_stream")
 
 
 class MoeError(RuntimeError):
@@ -78,6 +78,8 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
                                      Policy, vp, ctypes.POINTER(RoutingC), vp, vp, sz, vp]
     lib.moe_status_string.restype = ctypes.c_char_p
     lib.moe_status_string.argtypes = [c_int]
+    lib.moe_read_stream.restype = c_int
+    lib.moe_read_stream.argtypes = [vp, sz, vp, vp]
     if path is None:
         _lib = lib
     return lib
@@ -182,6 +184,14 @@ def moe_select(logits, policy: Policy, routing: Routing, stream=None):
         raise ValueError("routing buffers do not match B, E, k")
     r = routing.c_struct()
     _check(load().moe_select(_ptr(logits), B, E, policy, ctypes.byref(r), _stream(stream)))
+
+
+def moe_read_stream(src, out, stream=None):
+    """Read-only scan of the whole of `src` (a contiguous device tensor whose
+    byte size is a multiple of 16); out: int32/uint32 device tensor of 1024
+    words receiving each workgroup's XOR. A measurement utility."""
+    _check(load().moe_read_stream(_ptr(src), src.numel() * src.element_size(), _ptr(out),
+                                  _stream(stream)))
 
 
 def moe_expert_ffn(x, w_gate, w_up, w_down, routing: Routing, y, workspace, stream=None):

@@ -164,6 +164,12 @@ moe_status_t moe_layer_decode(const void *x, const void *w_g, const float *bias,
                                       y, ws, plan, s));
 }
 
+moe_status_t moe_read_stream(const void *src, size_t bytes, uint32_t *out, void *stream) {
+  if (!src || !aligned(src, 16) || !out || !aligned(out, 4) || bytes == 0 || bytes % 16)
+    return MOE_ERR_INVALID_ARG;
+  return hip_status(launch_read_stream(src, bytes, out, static_cast<hipStream_t>(stream)));
+}
+
 const char *moe_status_string(moe_status_t status) {
   switch (status) {
     case MOE_OK:

@@ -102,6 +102,11 @@ hipError_t launch_route_select(const void *x, const void *w_g, const float *bias
                                int E, float *logits, uint32_t *cnt, moe_policy_t p,
                                const moe_routing_t &r, hipStream_t s);
 
+// Read-only scan of `bytes` (a multiple of 16) at src by kReadStreamBlocks
+// workgroups; out[b] receives workgroup b's XOR of the words it read.
+constexpr int kReadStreamBlocks = 1024;
+hipError_t launch_read_stream(const void *src, size_t bytes, uint32_t *out, hipStream_t s);
+
 hipError_t launch_expert_ffn(const void *x, const void *w_gate, const void *w_up,
                              const void *w_down, moe_dtype_t dt, int B, int d, int E, int I,
                              int k, const moe_routing_t &r, void *y, char *ws,

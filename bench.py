@@ -51,6 +51,9 @@ def _parse():
                     help="run every configured (config, B, policy) case; one JSON line each to this file")
     ap.add_argument("--ffn-only", type=int, default=0, metavar="N",
                     help="run N eager moe_expert_ffn calls on rotating replicas and exit (for counter runs)")
+    ap.add_argument("--read-ceiling", type=float, default=0.0, metavar="MB",
+                    help="time a read-only reduction over MB megabytes (8 rotating buffers) and exit: "
+                         "the achievable HBM read rate on this GPU")
     ap.add_argument("--copy-calibration", type=float, default=0.0, metavar="MB",
                     help="run a plain device copy of MB megabytes 10 times and exit (counter scale)")
     return ap.parse_args()
@@ -268,6 +271,32 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    if args.read_ceiling:
+        # Eight distinct buffers in rotation, so the 256 MB Infinity Cache
+        # cannot serve one reduction from the previous one.
+        from aware_expert_routing_amd import _lib as L
+        n = int(args.read_ceiling * 1e6) // 16 * 4
+        bufs = [torch.ones(n, dtype=torch.float32, device="cuda") for _ in range(8)]
+        out = torch.empty((), dtype=torch.float32, device="cuda")
+        words = torch.empty(1024, dtype=torch.int32, device="cuda")
+        reps = 40
+        for name, fn in (("moe_read_stream (16-byte loads, 1024 workgroups)",
+                          lambda b: L.moe_read_stream(b, words)),
+                         ("torch.sum (read-only reduction)", lambda b: torch.sum(b, dim=0, out=out))):
+            for b in bufs:
+                fn(b)
+            ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            ev0.record()
+            for i in range(reps):
+                fn(bufs[i % 8])
+            ev1.record()
+            torch.cuda.synchronize()
+            ms = ev0.elapsed_time(ev1) / reps
+            print(json.dumps({"read_only_bytes": n * 4, "us_per_pass": round(ms * 1e3, 2),
+                              "read_GBps": round(n * 4 / (ms * 1e-3) / 1e9, 1), "passes": reps,
+                              "kernel": name}))
+        return
     if args.copy_calibration:
         n = int(args.copy_calibration * 1e6) // 4
         src = torch.ones(n, dtype=torch.float32, device="cuda")

@@ -156,6 +156,15 @@ moe_status_t moe_layer_decode(const void *x, const void *w_g, const float *bias,
 /* Static description of a status code. Never NULL. */
 const char *moe_status_string(moe_status_t status);
 
+/* Measurement utility, not a step of the layer: a read-only scan of `bytes`
+ * bytes at device pointer `src` (16-byte aligned, bytes a positive multiple
+ * of 16) by 1024 workgroups, each reading one contiguous block with 16-byte
+ * loads; out[1024] (device, uint32) receives each workgroup's XOR of the
+ * words it read. Its rate is the plain-streaming read ceiling of the GPU that
+ * the expert FFN's rate is compared with. MOE_ERR_INVALID_ARG on a null or
+ * misaligned pointer or a bad size; nothing else is checked or written. */
+moe_status_t moe_read_stream(const void *src, size_t bytes, uint32_t *out, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

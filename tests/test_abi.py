@@ -173,3 +173,12 @@ def test_ffn_validation(lib):
     assert call(k=200) == L.MOE_ERR_INVALID_ARG
     assert call(I=12) == L.MOE_ERR_UNSUPPORTED
     assert call(wsb=100) == L.MOE_ERR_WORKSPACE
+
+
+def test_read_stream_validation(lib):
+    st = L.MOE_ERR_INVALID_ARG
+    assert lib.moe_read_stream(None, 1024, A, None) == st
+    assert lib.moe_read_stream(A + 8, 1024, A, None) == st   # misaligned source
+    assert lib.moe_read_stream(A, 0, A, None) == st          # empty
+    assert lib.moe_read_stream(A, 1000, A, None) == st       # not a multiple of 16
+    assert lib.moe_read_stream(A, 1024, None, None) == st    # no output

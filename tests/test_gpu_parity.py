@@ -358,3 +358,24 @@ def test_unselected_experts_are_not_read():
     assert torch.equal(y2, y)
     del g2, u2, d2, dev2
     torch.cuda.empty_cache()
+
+
+def test_read_stream_reads_every_word():
+    """moe_read_stream (the read-ceiling utility) folds exactly the words of
+    each workgroup's contiguous block: its 1024 outputs equal the XOR of the
+    same blocks computed on the host."""
+    n16 = 1024 * 37 + 5  # 16-byte units, ragged over 1024 blocks
+    g = np.random.default_rng(7)
+    host = g.integers(0, 2**32, size=n16 * 4, dtype=np.uint64).astype(np.uint32)
+    src = torch.from_numpy(host.view(np.int32)).cuda()
+    out = torch.zeros(1024, dtype=torch.int32, device="cuda")
+    L.moe_read_stream(src, out)
+    torch.cuda.synchronize()
+    per = -(-n16 // 1024)
+    words = host.reshape(n16, 4)
+    want = np.zeros(1024, dtype=np.uint32)
+    for b in range(1024):
+        blk = words[b * per:min((b + 1) * per, n16)]
+        if len(blk):
+            want[b] = np.bitwise_xor.reduce(blk.reshape(-1))
+    assert np.array_equal(out.cpu().numpy().view(np.uint32), want)
