@@ -42,6 +42,16 @@ Readings where the pages are silent (each is stated where it is used):
   R6  SwiGLU expert: y = (SiLU(x G) * (x U)) D with SiLU(z) = z / (1 + e^-z),
       no biases; G, U are [d, I] and D is [I, d] per expert.
   R7  Empty slots (a token with fewer than k experts) carry id -1, weight 0.
+  R8  hier(m, m_r, g) for speculative batches ([XShare] summary and
+      abstract name a hierarchical, correlation-aware selection for
+      speculative decoding without giving its steps): tokens come in
+      requests of g consecutive tokens (the drafts of one request). The batch
+      keeps the budget(m) set S_b; each request r then keeps the m_r experts
+      of S_b with the largest softmax mass summed over its own tokens (in
+      token order, ranked as float32, ties to the lower index): S_r; each of
+      its tokens takes the first min(k, m_r) experts of its own order inside
+      S_r. Both levels maximise the total gating score under their budget,
+      the modular objective of [XShare].
 
 Parity status of each function is listed in its docstring ("pinned by ...").
 """
@@ -53,6 +63,7 @@ POLICY_TOPK = "topk"
 POLICY_OEA = "oea"
 POLICY_BUDGET = "budget"
 POLICY_GREEDY = "greedy"
+POLICY_HIER = "hier"
 
 
 # ---------------------------------------------------------------- precision
@@ -257,8 +268,51 @@ def select_greedy(L32: np.ndarray, k: int, m: int) -> np.ndarray:
     return _ids_matrix([_first_in(token_order(l), S, k) for l in L32], k)
 
 
-def select(L32: np.ndarray, policy: str, k: int, k0: int = 0, m: int = 0):
-    """Dispatch on policy name. Returns (ids [B,k] int32, mass or None)."""
+def request_sets(L32: np.ndarray, m: int, m_r: int, g: int, mass=None) -> np.ndarray:
+    """hier(m, m_r, g), the request level (reading R8): boolean [R, E], row r
+    the m_r experts of the batch's budget(m) set with the largest mass summed
+    over request r's tokens r*g .. r*g+g-1 (the last request may be shorter),
+    decided on float32-rounded sums, ties to the lower index.
+
+    Pinned by: brute force over every m_r-subset of S_b (each row maximises
+    the request's total gating score); m_r = m gives S_b for every request;
+    one request (g >= B) gives budget(m_r); rows lie inside S_b.
+    """
+    B, E = L32.shape
+    if not 1 <= m <= E or not 1 <= m_r <= m or g < 1:
+        raise ValueError("need 1 <= m_r <= m <= E and g >= 1")
+    if mass is None:
+        mass = budget_mass(L32)
+    Sb = budget_set(mass, m)
+    R = -(-B // g)
+    out = np.zeros((R, E), dtype=bool)
+    for r in range(R):
+        Mr = np.zeros(E, dtype=np.float64)
+        for t in range(r * g, min(B, r * g + g)):
+            Mr += softmax_row(np.asarray(L32[t], dtype=np.float32).astype(np.float64))
+        m32 = Mr.astype(np.float32).astype(np.float64)
+        cand = [e for e in range(E) if Sb[e]]
+        cand.sort(key=lambda e: (-m32[e], e))
+        out[r, cand[:m_r]] = True
+    return out
+
+
+def select_hier(L32: np.ndarray, k: int, m: int, m_r: int, g: int, mass=None) -> np.ndarray:
+    """hier(m, m_r, g) (reading R8): each token takes the first min(k, m_r)
+    experts of its own order inside its request's set. ids [B, k], -1 padded.
+
+    Pinned by: g = 1 with m_r >= k equals budget(m); g >= B equals
+    budget(m_r); m_r = m equals budget(m) for any g; each token's selection
+    is the top of its own order inside its request's set.
+    """
+    S = request_sets(L32, m, m_r, g, mass)
+    return _ids_matrix([_first_in(token_order(l), S[t // g], k) for t, l in enumerate(L32)], k)
+
+
+def select(L32: np.ndarray, policy: str, k: int, k0: int = 0, m: int = 0, g: int = 0):
+    """Dispatch on policy name. Returns (ids [B,k] int32, mass or None).
+    hier takes m (batch budget), k0 (the request budget m_r) and g (tokens per
+    request)."""
     L32 = np.asarray(L32, dtype=np.float32)
     _finite(L32)
     B, E = L32.shape
@@ -273,6 +327,9 @@ def select(L32: np.ndarray, policy: str, k: int, k0: int = 0, m: int = 0):
         return select_budget(L32, k, m, M), M
     if policy == POLICY_GREEDY:
         return select_greedy(L32, k, m), None
+    if policy == POLICY_HIER:
+        M = budget_mass(L32)
+        return select_hier(L32, k, m, k0, g, M), M
     raise ValueError(policy)
 
 
@@ -377,12 +434,12 @@ def expert_ffn(x, ids, W, w_gate, w_up, w_down, dtype: str, tokens=None) -> np.n
 # ------------------------------------------------------------------- layer
 
 def moe_layer(x, w_g, bias, w_gate, w_up, w_down, dtype: str, policy: str,
-              k: int, k0: int = 0, m: int = 0, tokens=None) -> dict:
+              k: int, k0: int = 0, m: int = 0, tokens=None, g: int = 0) -> dict:
     """The whole decode MoE layer: router, selection, weights, compaction,
     expert FFN. Selection runs on the float32-rounded logits (reading R2)."""
     L = router_logits(x, w_g, bias, dtype)
     L32 = L.astype(np.float32)
-    ids, mass = select(L32, policy, k, k0, m)
+    ids, mass = select(L32, policy, k, k0, m, g)
     W = gate_weights(L32, ids)
     c = compact(ids, L.shape[1])
     y = expert_ffn(x, ids, W, w_gate, w_up, w_down, dtype, tokens)

@@ -358,3 +358,67 @@ def test_invalid_policy_arguments():
     bad[0, 0] = np.nan
     with pytest.raises(ValueError):
         orc.select(bad, "topk", 4)
+
+
+# --------------------------------------------------------- hier (speculative)
+
+@pytest.mark.parametrize("seed", range(4))
+def test_hier_request_sets_brute_force(seed):
+    """Each request's set maximises the request's total gating score over
+    every m_r-subset of the batch set S_b, and lies inside S_b."""
+    B, E, g = 6, 8, 3
+    L = make_logits(B, E, seed=seed)
+    P = sp_softmax(L.astype(np.float64), axis=1)
+    for m in (3, 5, 8):
+        Sb = np.flatnonzero(orc.budget_set(orc.budget_mass(L), m)).tolist()
+        for m_r in range(1, m + 1):
+            S = orc.request_sets(L, m, m_r, g)
+            assert S.shape == (2, E)
+            for r in range(2):
+                toks = range(r * g, r * g + g)
+                got = np.flatnonzero(S[r]).tolist()
+                assert len(got) == m_r and set(got) <= set(Sb)
+                score = lambda c: sum(P[t, e] for t in toks for e in c)
+                best = max(score(c) for c in itertools.combinations(Sb, m_r))
+                assert score(got) >= best - 1e-12
+
+
+@pytest.mark.parametrize("seed", range(3))
+def test_hier_reductions(seed):
+    """g = 1 with m_r >= k is budget(m); one request (g >= B) is budget(m_r);
+    m_r = m is budget(m) for any g."""
+    B, E, k = 12, 32, 4
+    L = make_logits(B, E, seed=10 + seed)
+    for m in (4, 10, 32):
+        bm = orc.select_budget(L, k, m)
+        for m_r in range(k, m + 1):
+            assert np.array_equal(orc.select_hier(L, k, m, m_r, 1), bm)
+        for m_r in range(1, m + 1):
+            assert np.array_equal(orc.select_hier(L, k, m, m_r, B), orc.select_budget(L, k, m_r))
+            assert np.array_equal(orc.select_hier(L, k, m, m_r, B + 5), orc.select_budget(L, k, m_r))
+        for g in (1, 2, 5, 12):
+            assert np.array_equal(orc.select_hier(L, k, m, m, g), bm)
+
+
+def test_hier_tokens_take_their_own_top_inside_request_set():
+    """Every token's ids are the first min(k, m_r) of its own order inside its
+    request's set; the ragged last request is handled; padding is -1."""
+    B, E, k, g = 10, 16, 4, 4
+    L = make_logits(B, E, seed=21)
+    for m, m_r in ((8, 2), (8, 5), (16, 16), (6, 6)):
+        ids = orc.select_hier(L, k, m, m_r, g)
+        S = orc.request_sets(L, m, m_r, g)
+        assert S.shape[0] == 3
+        for t in range(B):
+            order = sorted(range(E), key=lambda e: (-float(L[t, e]), e))
+            want = [e for e in order if S[t // g, e]][:min(k, m_r)]
+            assert ids[t, :len(want)].tolist() == want
+            assert (ids[t, len(want):] == -1).all()
+
+
+def test_hier_argument_checks():
+    L = make_logits(4, 8, seed=1)
+    with pytest.raises(ValueError):
+        orc.request_sets(L, 4, 5, 2)   # m_r > m
+    with pytest.raises(ValueError):
+        orc.request_sets(L, 4, 2, 0)   # g < 1
