@@ -27,6 +27,7 @@ MOE_POLICY_TOPK = 0
 MOE_POLICY_OEA = 1
 MOE_POLICY_BUDGET = 2
 MOE_POLICY_GREEDY = 3
+MOE_POLICY_HIER = 4
 
 EXPORTS = ("moe_workspace_bytes", "moe_route", "moe_select", "moe_expert_ffn",
            "moe_layer_decode", "moe_status_string", "moe_read_stream")
@@ -40,7 +41,7 @@ class MoeError(RuntimeError):
 
 class Policy(ctypes.Structure):
     _fields_ = [("kind", ctypes.c_int32), ("k", ctypes.c_int32), ("k0", ctypes.c_int32),
-                ("m", ctypes.c_int32)]
+                ("m", ctypes.c_int32), ("g", ctypes.c_int32)]
 
 
 _ROUTING_FIELDS = ("topk_ids", "topk_w", "n_active", "active_experts", "expert_offsets",
@@ -94,12 +95,14 @@ def _check(status: int):
         raise MoeError(status, status_string(status))
 
 
-def make_policy(kind: str, k: int, k0: int = 0, m: int = 0) -> Policy:
+def make_policy(kind: str, k: int, k0: int = 0, m: int = 0, g: int = 0) -> Policy:
+    """kind: topk | oea (k0) | budget (m) | greedy (m) | hier (m, k0 = request
+    budget m_r, g = tokens per request)."""
     kinds = {"topk": MOE_POLICY_TOPK, "oea": MOE_POLICY_OEA, "budget": MOE_POLICY_BUDGET,
-             "greedy": MOE_POLICY_GREEDY}
+             "greedy": MOE_POLICY_GREEDY, "hier": MOE_POLICY_HIER}
     if kind not in kinds:
         raise ValueError(f"unknown policy {kind!r}")
-    return Policy(kinds[kind], int(k), int(k0), int(m))
+    return Policy(kinds[kind], int(k), int(k0), int(m), int(g))
 
 
 # ----------------------------------------------------------- torch helpers

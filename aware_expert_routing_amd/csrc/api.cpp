@@ -32,6 +32,9 @@ moe_status_t check_policy(const moe_policy_t &p, int E) {
     case MOE_POLICY_BUDGET:
     case MOE_POLICY_GREEDY:
       return (p.m >= 1 && p.m <= E) ? MOE_OK : MOE_ERR_INVALID_ARG;
+    case MOE_POLICY_HIER:
+      return (p.m >= 1 && p.m <= E && p.k0 >= 1 && p.k0 <= p.m && p.g >= 1) ? MOE_OK
+                                                                             : MOE_ERR_INVALID_ARG;
     default:
       return MOE_ERR_INVALID_ARG;
   }
@@ -106,7 +109,7 @@ moe_status_t moe_select(const float *logits, int B, int E, moe_policy_t policy,
   if (B < 1 || E < 1) return MOE_ERR_INVALID_ARG;
   if (B > kMaxB || E > kMaxE) return MOE_ERR_UNSUPPORTED;
   MOE_TRY(check_policy(policy, E));
-  MOE_TRY(check_routing(out, policy.kind == MOE_POLICY_BUDGET));
+  MOE_TRY(check_routing(out, policy.kind == MOE_POLICY_BUDGET || policy.kind == MOE_POLICY_HIER));
   hipStream_t s = static_cast<hipStream_t>(stream);
   return hip_status(launch_select(logits, B, E, policy, *out, s));
 }
@@ -146,7 +149,7 @@ moe_status_t moe_layer_decode(const void *x, const void *w_g, const float *bias,
   MOE_TRY(check_dense(y));
   if (!logits || !aligned(logits, 4)) return MOE_ERR_INVALID_ARG;
   if (bias && !aligned(bias, 4)) return MOE_ERR_INVALID_ARG;
-  MOE_TRY(check_routing(routing, policy.kind == MOE_POLICY_BUDGET));
+  MOE_TRY(check_routing(routing, policy.kind == MOE_POLICY_BUDGET || policy.kind == MOE_POLICY_HIER));
   const Workspace plan = plan_workspace(B, d, E, I, policy.k, dt);
   MOE_TRY(check_workspace(workspace, workspace_bytes, plan.total));
   hipStream_t s = static_cast<hipStream_t>(stream);

@@ -17,7 +17,7 @@ template <bool VEC, int NV, int TPW>
 __global__ __launch_bounds__(kThreads) void route_select_kernel(
     const uint16_t *__restrict__ x, const uint16_t *__restrict__ w, const float *__restrict__ bias,
     int B, int d, int E, float *__restrict__ logits, uint32_t *__restrict__ cnt, int kind, int k,
-    int k0, int m, int32_t *__restrict__ topk_ids, float *__restrict__ topk_w,
+    int k0, int m, int g, int32_t *__restrict__ topk_ids, float *__restrict__ topk_w,
     int32_t *__restrict__ n_active, int32_t *__restrict__ active_experts,
     int32_t *__restrict__ expert_offsets, int32_t *__restrict__ pair_token,
     int32_t *__restrict__ pair_slot, float *__restrict__ batch_mass) {
@@ -34,7 +34,7 @@ __global__ __launch_bounds__(kThreads) void route_select_kernel(
   }
   __syncthreads();
   if (!s_last) return;
-  select_block<NV, TPW>(logits, B, E, kind, k, k0, m, topk_ids, topk_w, n_active, active_experts,
+  select_block<NV, TPW>(logits, B, E, kind, k, k0, m, g, topk_ids, topk_w, n_active, active_experts,
                    expert_offsets, pair_token, pair_slot, batch_mass);
 }
 
@@ -42,10 +42,10 @@ template <bool VEC>
 void launch_rs(dim3 grid, const uint16_t *x, const uint16_t *w, const float *bias, int B, int d,
                int E, float *logits, uint32_t *cnt, const moe_policy_t &p, const moe_routing_t &r,
                hipStream_t s) {
-  float *mass = p.kind == MOE_POLICY_BUDGET ? r.batch_mass : nullptr;
+  float *mass = (p.kind == MOE_POLICY_BUDGET || p.kind == MOE_POLICY_HIER) ? r.batch_mass : nullptr;
   dispatch_select_shape(B, E, [&](auto nv, auto tpw) {
     route_select_kernel<VEC, decltype(nv)::value, decltype(tpw)::value><<<grid, kThreads, 0, s>>>(
-        x, w, bias, B, d, E, logits, cnt, p.kind, p.k, p.k0, p.m, r.topk_ids, r.topk_w,
+        x, w, bias, B, d, E, logits, cnt, p.kind, p.k, p.k0, p.m, p.g, r.topk_ids, r.topk_w,
         r.n_active, r.active_experts, r.expert_offsets, r.pair_token, r.pair_slot, mass);
   });
 }

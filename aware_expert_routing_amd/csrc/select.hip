@@ -7,12 +7,12 @@ namespace {
 
 template <int NV, int TPW>
 __global__ __launch_bounds__(kThreads) void select_kernel(
-    const float *__restrict__ logits, int B, int E, int kind, int k, int k0, int m,
+    const float *__restrict__ logits, int B, int E, int kind, int k, int k0, int m, int g,
     int32_t *__restrict__ topk_ids, float *__restrict__ topk_w, int32_t *__restrict__ n_active,
     int32_t *__restrict__ active_experts, int32_t *__restrict__ expert_offsets,
     int32_t *__restrict__ pair_token, int32_t *__restrict__ pair_slot,
     float *__restrict__ batch_mass) {
-  select_block<NV, TPW>(logits, B, E, kind, k, k0, m, topk_ids, topk_w, n_active, active_experts,
+  select_block<NV, TPW>(logits, B, E, kind, k, k0, m, g, topk_ids, topk_w, n_active, active_experts,
                    expert_offsets, pair_token, pair_slot, batch_mass);
 }
 
@@ -20,10 +20,10 @@ __global__ __launch_bounds__(kThreads) void select_kernel(
 
 hipError_t launch_select(const float *logits, int B, int E, moe_policy_t p,
                          const moe_routing_t &r, hipStream_t s) {
-  float *mass = p.kind == MOE_POLICY_BUDGET ? r.batch_mass : nullptr;
+  float *mass = (p.kind == MOE_POLICY_BUDGET || p.kind == MOE_POLICY_HIER) ? r.batch_mass : nullptr;
   dispatch_select_shape(B, E, [&](auto nv, auto tpw) {
     select_kernel<decltype(nv)::value, decltype(tpw)::value><<<1, kThreads, 0, s>>>(
-        logits, B, E, p.kind, p.k, p.k0, p.m, r.topk_ids, r.topk_w, r.n_active,
+        logits, B, E, p.kind, p.k, p.k0, p.m, p.g, r.topk_ids, r.topk_w, r.n_active,
         r.active_experts, r.expert_offsets, r.pair_token, r.pair_slot, mass);
   });
   return hipGetLastError();

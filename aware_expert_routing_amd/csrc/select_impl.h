@@ -19,6 +19,12 @@
 //             gain of e is sum_t max(0, p_t[e] - thr_t), thr_t being t's k-th
 //             largest probability in S (0 while t has fewer than k there);
 //             ties to the lower index.
+//   HIER(m, m_r, g)  "XShare", summary and abstract (hierarchical selection
+//             for speculative batches; the steps are this build's reading):
+//             the batch keeps the BUDGET(m) set; request r (tokens r*g ..
+//             r*g+g-1) keeps the m_r experts of that set with the largest
+//             mass summed over its own tokens, in token order (ties to the
+//             lower index); its tokens rank inside that request set.
 //   weights   softmax over each token's selected logits.
 //   compact   "Lynx", Technical Summary 2.2: the batch activates one
 //             consolidated expert set; this kernel lists it (ascending) and
@@ -178,12 +184,13 @@ __device__ __forceinline__ bool bit_of(const uint32_t *mask, int e) { return (ma
 // phases are unrolled over the slots, so a small TPW keeps the code small.
 template <int NV, int TPW>
 __device__ __forceinline__ void select_block(
-    const float *__restrict__ logits, int B, int E, int kind, int k, int k0, int m,
+    const float *__restrict__ logits, int B, int E, int kind, int k, int k0, int m, int g,
     int32_t *__restrict__ topk_ids, float *__restrict__ topk_w, int32_t *__restrict__ n_active,
     int32_t *__restrict__ active_experts, int32_t *__restrict__ expert_offsets,
     int32_t *__restrict__ pair_token, int32_t *__restrict__ pair_slot,
     float *__restrict__ batch_mass) {
   __shared__ uint32_t allowed[kWords];
+  __shared__ uint32_t req_allowed[kMaxB][kWords];  // HIER: each request's set
   __shared__ uint32_t etok[kMaxE][kTokWords];  // bit t of etok[e]: token t routes to e
   __shared__ int16_t sel_id[kMaxB][kMaxK];
   __shared__ float sel_w[kMaxB][kMaxK];
@@ -213,6 +220,8 @@ __device__ __forceinline__ void select_block(
     allowed[i] = full;
   }
   for (int i = tid; i < kMaxE * kTokWords; i += kThreads) etok[i / kTokWords][i % kTokWords] = 0;
+  if (kind == MOE_POLICY_HIER)
+    for (int i = tid; i < ((B + g - 1) / g) * kWords; i += kThreads) req_allowed[i / kWords][i % kWords] = 0;
 
   // Phase 1: logits into registers. Addresses are clamped so that every load
   // is in bounds; values outside [B, E) are never used as candidates.
@@ -260,7 +269,7 @@ __device__ __forceinline__ void select_block(
         if (lane < n) atomicOr(&allowed[pick_e[ti] >> 5], 1u << (pick_e[ti] & 31));
       }
     }
-  } else if (kind == MOE_POLICY_BUDGET) {
+  } else if (kind == MOE_POLICY_BUDGET || kind == MOE_POLICY_HIER) {
     // Per-token softmax over all E experts, then column sums over the batch
     // in a fixed order (token slot ti outer, wave inner).
     float macc = 0.0f;  // thread tid < E accumulates expert tid
@@ -300,6 +309,50 @@ __device__ __forceinline__ void select_block(
         rank += (o > macc) || (o == macc && e2 < tid);
       }
       if (rank < m) atomicOr(&allowed[tid >> 5], 1u << (tid & 31));
+    }
+    if (kind == MOE_POLICY_HIER) {
+      // Request level: wave w takes requests w, w+16, ...; a request's mass
+      // is summed over its tokens in order (each token's softmax recomputed
+      // from the logits by the same expression as above), then ranked inside
+      // the batch set with the same wave ranking as the tokens (k0 = m_r).
+      __syncthreads();  // the batch set is complete
+      const int R = (B + g - 1) / g;
+      for (int r = wave; r < R; r += kWaves) {
+        float Mr[NV];
+#pragma unroll
+        for (int v = 0; v < NV; ++v) Mr[v] = 0.0f;
+        const int t1 = min(B, r * g + g);
+        for (int t = r * g; t < t1; ++t) {
+          float lv[NV];
+#pragma unroll
+          for (int v = 0; v < NV; ++v)
+            lv[v] = __hip_atomic_load(const_cast<float *>(logits) + t * E + min(lane + 64 * v, E - 1),
+                                      __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          float mx = -INFINITY;
+#pragma unroll
+          for (int v = 0; v < NV; ++v)
+            if (lane + 64 * v < E) mx = fmaxf(mx, lv[v]);
+          mx = wave_maxf(mx);
+          float sm = 0.0f;
+#pragma unroll
+          for (int v = 0; v < NV; ++v)
+            if (lane + 64 * v < E) sm += expf(lv[v] - mx);
+          sm = wave_sum(sm);
+#pragma unroll
+          for (int v = 0; v < NV; ++v)
+            if (lane + 64 * v < E) Mr[v] += expf(lv[v] - mx) / sm;
+        }
+        uint32_t key[NV];
+#pragma unroll
+        for (int v = 0; v < NV; ++v) {
+          const int e = lane + 64 * v;
+          key[v] = (e < E && bit_of(allowed, e)) ? ord_bits(Mr[v]) : 0u;
+        }
+        int pe = 0;
+        uint32_t pk = 0, ptop = 0;
+        const int n = wave_rank<NV>(key, k0, 0, lane, pe, pk, ptop);
+        if (lane < n) atomicOr(&req_allowed[r][pe >> 5], 1u << (pe & 31));
+      }
     }
   } else if (kind == MOE_POLICY_GREEDY) {
     // Per-token softmax normalisers (probabilities are recomputed from the
@@ -435,10 +488,11 @@ __device__ __forceinline__ void select_block(
     const int t = wave + kWaves * ti;
     if (t < B) {
       uint32_t key[NV];
+      const uint32_t *mask = kind == MOE_POLICY_HIER ? req_allowed[t / g] : allowed;
 #pragma unroll
       for (int v = 0; v < NV; ++v) {
         const int e = lane + 64 * v;
-        key[v] = (e < E && bit_of(allowed, e) && !((picked[ti] >> v) & 1u)) ? ord_bits(L[ti][v]) : 0u;
+        key[v] = (e < E && bit_of(mask, e) && !((picked[ti] >> v) & 1u)) ? ord_bits(L[ti][v]) : 0u;
       }
       // Continue after the picks phase 2 already made (none unless OEA).
       int e = pick_e[ti];

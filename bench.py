@@ -40,9 +40,10 @@ def _parse():
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--config", default="qwen3_30b_bf16")
     ap.add_argument("--batch", type=int, default=16)
-    ap.add_argument("--policy", default="oea", choices=["topk", "oea", "budget"])
+    ap.add_argument("--policy", default="oea", choices=["topk", "oea", "budget", "greedy", "hier"])
     ap.add_argument("--k0", type=int, default=4)
     ap.add_argument("--m", type=int, default=32)
+    ap.add_argument("--g", type=int, default=4, help="hier: tokens per request (--k0 is the request budget)")
     ap.add_argument("--rotate-bytes", type=float, default=2.0e9,
                     help="replicas are added until they hold this many distinct active bytes")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
@@ -67,12 +68,12 @@ def _percentiles(v):
 class Case:
     """Device state for one (config, B, policy) workload."""
 
-    def __init__(self, cfg, B, policy, k0, m, inp, dev_base, rotate_bytes):
+    def __init__(self, cfg, B, policy, k0, m, inp, dev_base, rotate_bytes, g=0):
         import torch
         from aware_expert_routing_amd import _lib as L
 
         self.cfg, self.B = cfg, B
-        self.policy = L.make_policy(policy, cfg.k, k0, m)
+        self.policy = L.make_policy(policy, cfg.k, k0, m, g)
         self.policy_name = policy
         self.k0, self.m = k0, m
         tdt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
@@ -174,18 +175,19 @@ def _traffic(workload):
     return int(t["fetch_bytes"] + t["write_bytes"])
 
 
-def _cpu_baseline(cfg, inp, B, policy, k0, m, active_bytes, seconds):
+def _cpu_baseline(cfg, inp, B, policy, k0, m, active_bytes, seconds, g=0):
     from threadpoolctl import threadpool_info
     from oracle import moe_oracle as orc
 
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     args = (inp["x"][:B], inp["w_g"], inp["bias"], inp["w_gate"], inp["w_up"], inp["w_down"],
             cfg.dtype, policy, cfg.k, k0, m)
+    kw = {"g": g}
     times = []
     t_end = time.perf_counter() + seconds
     while True:
         t0 = time.perf_counter()
-        orc.moe_layer(*args)
+        orc.moe_layer(*args, **kw)
         times.append(time.perf_counter() - t0)
         if time.perf_counter() > t_end or len(times) >= 200:
             break
@@ -196,10 +198,15 @@ def _cpu_baseline(cfg, inp, B, policy, k0, m, active_bytes, seconds):
                       f"median {med * 1e3:.1f} ms per call"}
 
 
-def _run_case(cfg, B, policy, k0, m, inp, dev, args, with_cpu):
+def _policy_name(policy, k0, m, g):
+    return policy + {"oea": f"(k0={k0})", "budget": f"(m={m})", "greedy": f"(m={m})",
+                     "hier": f"(m={m},m_r={k0},g={g})"}.get(policy, "")
+
+
+def _run_case(cfg, B, policy, k0, m, inp, dev, args, with_cpu, g=0):
     import torch
 
-    c = Case(cfg, B, policy, k0, m, inp, dev, args.rotate_bytes)
+    c = Case(cfg, B, policy, k0, m, inp, dev, args.rotate_bytes, g)
     R = len(c.replicas)
     per, total = _time_steps(c.layer, R, args.steps, args.warmup)
     med, p10, p90 = _percentiles(per)
@@ -209,7 +216,7 @@ def _run_case(cfg, B, policy, k0, m, inp, dev, args, with_cpu):
     ffn_ms = total_f / args.steps
     value = c.active_bytes / (ms_per_step * 1e-3) / 1e9
     ffn_gbps = c.active_bytes / (ffn_ms * 1e-3) / 1e9
-    pol = policy + (f"(k0={k0})" if policy == "oea" else f"(m={m})" if policy == "budget" else "")
+    pol = _policy_name(policy, k0, m, g)
     out_workload = (f"{cfg.name} decode MoE layer, B={B}, d={cfg.d}, E={cfg.E}, k={cfg.k}, "
                     f"I={cfg.I}, policy {pol}")
     out = {
@@ -241,7 +248,7 @@ def _run_case(cfg, B, policy, k0, m, inp, dev, args, with_cpu):
                      "bytes_per_launch": c.active_bytes},
     }
     if with_cpu:
-        out["cpu_baseline"] = _cpu_baseline(cfg, inp, B, policy, k0, m, c.active_bytes, args.cpu_seconds)
+        out["cpu_baseline"] = _cpu_baseline(cfg, inp, B, policy, k0, m, c.active_bytes, args.cpu_seconds, g)
     del c
     torch.cuda.empty_cache()
     return out
@@ -311,11 +318,13 @@ def main():
             for cname, cfg in CONFIGS.items():
                 inp = make_layer(cfg, max(cfg.batches))
                 dev = _upload(inp, cfg.dtype)
-                pols = [("topk", 0, 0)] + [("oea", k0, 0) for k0 in cfg.oea_k0] + \
-                       [("budget", 0, m) for m in cfg.budget_m]
+                pols = [("topk", 0, 0, 0)] + [("oea", k0, 0, 0) for k0 in cfg.oea_k0] + \
+                       [("budget", 0, m, 0) for m in cfg.budget_m]
+                if cname == "specdec_bf16":  # requests of 4 drafts
+                    pols += [("hier", m // 4, m, 4) for m in cfg.budget_m]
                 for B in cfg.batches:
-                    for pol, k0, m in pols:
-                        rec = _run_case(cfg, B, pol, k0, m, inp, dev, args, with_cpu=False)
+                    for pol, k0, m, g in pols:
+                        rec = _run_case(cfg, B, pol, k0, m, inp, dev, args, with_cpu=False, g=g)
                         f.write(json.dumps(rec) + "\n")
                         f.flush()
                         print(f"{cname} B={B} {pol}{k0 or m or ''}: n_active={rec['n_active']} "
@@ -328,7 +337,8 @@ def main():
     inp = make_layer(cfg, max(args.batch, max(cfg.batches)))
     dev = _upload(inp, cfg.dtype)
     if args.ffn_only:
-        c = Case(cfg, args.batch, args.policy, args.k0, args.m, inp, dev, args.rotate_bytes)
+        c = Case(cfg, args.batch, args.policy, args.k0, args.m, inp, dev, args.rotate_bytes,
+                 args.g if args.policy == "hier" else 0)
         for i in range(args.ffn_only):
             c.ffn(i % len(c.replicas))
         torch.cuda.synchronize()
@@ -336,7 +346,7 @@ def main():
                           "active_expert_bytes": c.active_bytes}), flush=True)
         return
     rec = _run_case(cfg, args.batch, args.policy, args.k0, args.m, inp, dev, args,
-                    with_cpu=not args.no_cpu_baseline)
+                    with_cpu=not args.no_cpu_baseline, g=args.g if args.policy == "hier" else 0)
     print(json.dumps(rec), flush=True)
 
 

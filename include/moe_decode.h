@@ -25,6 +25,16 @@
  *                              retained top-k softmax mass (ties to the lower
  *                              index), m experts in all; each token takes its
  *                              top min(k,m) inside it ("XShare", abstract).
+ *                   HIER(m, m_r, g)  speculative batches: tokens form requests
+ *                              of g consecutive tokens (one request's
+ *                              drafts); the batch keeps the BUDGET(m) set;
+ *                              each request keeps the m_r experts of it with
+ *                              the largest softmax mass summed over the
+ *                              request's tokens (ties to the lower index);
+ *                              each token takes its top min(k, m_r) inside
+ *                              its request's set ("XShare", summary and
+ *                              abstract: hierarchical selection for
+ *                              speculative decoding; this build's reading).
  *   4. weights:   gate weights are the softmax over each token's selected
  *                 logits (renormalised); empty slots weigh 0.
  *   5. compaction: the ascending list of active experts and, per active
@@ -82,15 +92,20 @@ typedef enum {
   MOE_POLICY_TOPK = 0,   /* k experts per token (k <= E)                         */
   MOE_POLICY_OEA = 1,    /* 1 <= k0 <= k; tokens get min(k, |S|) experts         */
   MOE_POLICY_BUDGET = 2, /* 1 <= m <= E; tokens get min(k, m) experts            */
-  MOE_POLICY_GREEDY = 3  /* 1 <= m <= E; tokens get min(k, m) experts            */
+  MOE_POLICY_GREEDY = 3, /* 1 <= m <= E; tokens get min(k, m) experts            */
+  MOE_POLICY_HIER = 4    /* 1 <= k0 = m_r <= m <= E, g >= 1; tokens get
+                            min(k, m_r) experts                                  */
 } moe_policy_kind_t;
 
-/* Selection policy. k0 is read only by OEA, m only by BUDGET and GREEDY. */
+/* Selection policy. k0 is read by OEA (its k0) and HIER (the request budget
+ * m_r); m by BUDGET, GREEDY and HIER (the batch budget); g only by HIER
+ * (tokens per request: token t belongs to request t / g). */
 typedef struct {
   int32_t kind; /* moe_policy_kind_t */
   int32_t k;
   int32_t k0;
   int32_t m;
+  int32_t g;
 } moe_policy_t;
 
 /* Routing outputs (device pointers, caller-owned, written in full by every
@@ -105,9 +120,9 @@ typedef struct {
   int32_t *pair_token;     /* [B*k] token of each (expert, token) pair, tokens
                                     ascending within an expert; then -1           */
   int32_t *pair_slot;      /* [B*k] slot j of that pair in topk_ids; then -1        */
-  float *batch_mass;       /* [E]   BUDGET: sum over tokens of softmax(logits_t);
-                                    may be NULL (other policies, GREEDY included,
-                                    leave it alone)                               */
+  float *batch_mass;       /* [E]   BUDGET and HIER: sum over tokens of
+                                    softmax(logits_t); may be NULL for the other
+                                    policies, which leave it alone               */
 } moe_routing_t;
 
 /* Bytes of workspace the calls below need for these sizes (256-byte aligned

@@ -53,15 +53,20 @@ class Guarded:
         return bool(torch.all(tail == float(self.fill)))
 
 
-def policy_args(policy: str, p: int):
+def policy_args(policy: str, p):
+    """Policy parameters as keyword arguments; p is k0 (oea), m (budget,
+    greedy) or the tuple (m, m_r, g) (hier: m_r travels as k0)."""
     if policy == "topk":
-        return dict(policy="topk", k0=0, m=0)
+        return dict(policy="topk", k0=0, m=0, g=0)
     if policy == "oea":
-        return dict(policy="oea", k0=p, m=0)
+        return dict(policy="oea", k0=p, m=0, g=0)
     if policy == "budget":
-        return dict(policy="budget", k0=0, m=p)
+        return dict(policy="budget", k0=0, m=p, g=0)
     if policy == "greedy":
-        return dict(policy="greedy", k0=0, m=p)
+        return dict(policy="greedy", k0=0, m=p, g=0)
+    if policy == "hier":
+        m, m_r, g = p
+        return dict(policy="hier", k0=m_r, m=m, g=g)
     raise ValueError(policy)
 
 

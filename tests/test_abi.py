@@ -98,6 +98,12 @@ def _layer(lib, **kw):
     (dict(pol=L.Policy(L.MOE_POLICY_BUDGET, 8, 0, 32), r=_routing(mass=False)), L.MOE_ERR_INVALID_ARG),
     (dict(pol=L.Policy(L.MOE_POLICY_GREEDY, 8, 0, 0)), L.MOE_ERR_INVALID_ARG),  # m < 1
     (dict(pol=L.Policy(L.MOE_POLICY_GREEDY, 8, 0, 129)), L.MOE_ERR_INVALID_ARG),  # m > E
+    (dict(pol=L.Policy(L.MOE_POLICY_HIER, 8, 4, 0, 4)), L.MOE_ERR_INVALID_ARG),   # m < 1
+    (dict(pol=L.Policy(L.MOE_POLICY_HIER, 8, 0, 32, 4)), L.MOE_ERR_INVALID_ARG),  # m_r < 1
+    (dict(pol=L.Policy(L.MOE_POLICY_HIER, 8, 33, 32, 4)), L.MOE_ERR_INVALID_ARG),  # m_r > m
+    (dict(pol=L.Policy(L.MOE_POLICY_HIER, 8, 8, 32, 0)), L.MOE_ERR_INVALID_ARG),  # g < 1
+    (dict(pol=L.Policy(L.MOE_POLICY_HIER, 8, 8, 129, 4)), L.MOE_ERR_INVALID_ARG),  # m > E
+    (dict(pol=L.Policy(L.MOE_POLICY_HIER, 8, 8, 32, 4), r=_routing(mass=False)), L.MOE_ERR_INVALID_ARG),
     (dict(pol=L.Policy(7, 8, 0, 0)), L.MOE_ERR_INVALID_ARG),
     (dict(ws=None), L.MOE_ERR_WORKSPACE),
     (dict(ws=A + 16), L.MOE_ERR_WORKSPACE),             # not 256-byte aligned

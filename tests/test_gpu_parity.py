@@ -39,10 +39,10 @@ def _dtype(cfg):
     return torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
 
 
-def _run_layer(cfg: LayerConfig, inp, dev, B: int, policy: str, k0: int, m: int, guard=True):
+def _run_layer(cfg: LayerConfig, inp, dev, B: int, policy: str, k0: int, m: int, guard=True, g: int = 0):
     tdt = _dtype(cfg)
     x = dev["x"][:B].contiguous()
-    pol = L.make_policy(policy, cfg.k, k0, m)
+    pol = L.make_policy(policy, cfg.k, k0, m, g)
     r = L.Routing(B, cfg.E, cfg.k)
     ws = L.alloc_workspace(B, cfg.d, cfg.E, cfg.I, cfg.k, tdt)
     lg = Guarded((B, cfg.E), torch.float32, -7.0)
@@ -75,19 +75,22 @@ def _assert_sync_words_clear(ws):
     assert not words[_TOK_CNT[0] // 4:_TOK_CNT[1] // 4].any(), "a per-token counter was left non-zero"
 
 
-def _oracle(cfg, inp, B, policy, k0, m, tokens=None):
+def _oracle(cfg, inp, B, policy, k0, m, tokens=None, g=0):
     return orc.moe_layer(inp["x"][:B], inp["w_g"], inp["bias"], inp["w_gate"], inp["w_up"],
-                         inp["w_down"], cfg.dtype, policy, cfg.k, k0, m, tokens=tokens)
+                         inp["w_down"], cfg.dtype, policy, cfg.k, k0, m, tokens=tokens, g=g)
 
 
 def _assert_routing_from_gpu_logits(Lg, rg, cfg, a):
     """The oracle's selection run on the GPU's own float32 logits reproduces
     the GPU routing bit for bit (budget ranks the GPU's batch masses, which
     must match the oracle's masses of the same logits to 2e-6 relative)."""
-    if a["policy"] == "budget":
+    if a["policy"] in ("budget", "hier"):
         M = orc.budget_mass(Lg)
         np.testing.assert_allclose(rg["mass"], M, rtol=2e-6, atol=1e-12, err_msg="batch_mass")
-        ids = orc.select_budget(Lg, cfg.k, a["m"], mass=rg["mass"])
+        if a["policy"] == "budget":
+            ids = orc.select_budget(Lg, cfg.k, a["m"], mass=rg["mass"])
+        else:
+            ids = orc.select_hier(Lg, cfg.k, a["m"], a["k0"], a["g"], mass=rg["mass"])
     else:
         ids, _ = orc.select(Lg, a["policy"], cfg.k, a["k0"], a["m"])
     o = {"ids": ids, "w": orc.gate_weights(Lg, ids)}
@@ -116,18 +119,28 @@ def _greedy_layer_cases():
                             ("specdec_bf16", 64, 32))]
 
 
-@pytest.mark.parametrize("cname,B,policy,p", _layer_cases() + _greedy_layer_cases())
+def _hier_layer_cases():
+    # (m, m_r, g): the speculative batch's own request structure (g = 4
+    # drafts per request), and other batches grouped for coverage.
+    return [pytest.param(c, B, "hier", p, id=f"{c}-B{B}-hier{p[0]}-{p[1]}-{p[2]}")
+            for c, B, p in (("specdec_bf16", 64, (48, 12, 4)), ("specdec_bf16", 64, (32, 8, 4)),
+                            ("specdec_bf16", 64, (64, 16, 4)), ("qwen3_30b_bf16", 16, (32, 8, 2)),
+                            ("qwen3_30b_bf16", 32, (48, 10, 4)), ("lynx_bf16", 16, (24, 10, 4)),
+                            ("tiny_f32", 4, (8, 4, 2)))]
+
+
+@pytest.mark.parametrize("cname,B,policy,p", _layer_cases() + _greedy_layer_cases() + _hier_layer_cases())
 def test_layer_matches_oracle(cname, B, policy, p):
     cfg = CONFIGS[cname]
     inp, dev = _layer_inputs(cname)
     a = policy_args(policy, p)
     print(f"\n[case] {cname} B={B} {policy}{p}", flush=True)
-    Lg, rg, y = _run_layer(cfg, inp, dev, B, a["policy"], a["k0"], a["m"])
+    Lg, rg, y = _run_layer(cfg, inp, dev, B, a["policy"], a["k0"], a["m"], g=a["g"])
     # Large layers: the oracle computes a sample of tokens one by one.
     tokens = None
     if cfg.d * cfg.I * B > 2048 * 768 * 64:
         tokens = sorted({0, 1, B // 2, B - 1})
-    o = _oracle(cfg, inp, B, a["policy"], a["k0"], a["m"], tokens)
+    o = _oracle(cfg, inp, B, a["policy"], a["k0"], a["m"], tokens, g=a["g"])
     assert_logits_close(Lg, o["logits"], cname)
     assert_routing_equal(rg, o, cname, weight_rtol_from_logits(Lg, o["logits"]))
     _assert_routing_from_gpu_logits(Lg, rg, cfg, a)
@@ -226,6 +239,9 @@ def _sel_policies(E, k, B):
     out += [("budget", m) for m in sorted({1, max(1, k - 1), max(1, E // 4), E})]
     if B * E <= 64 * 128:  # the oracle's greedy re-sorts per candidate: keep it small
         out += [("greedy", m) for m in sorted({1, max(1, k - 1), max(1, E // 4)})]
+    mb = max(1, E // 2)
+    out += [("hier", p) for p in sorted({(mb, max(1, min(mb, k // 2)), 2), (mb, min(mb, k + 2), 4),
+                                          (E, max(1, k - 1), 1), (mb, max(1, mb // 2), B)})]
     return out
 
 
@@ -234,7 +250,8 @@ def _sel_cases():
     for (B, E, k) in _SEL_SHAPES:
         for kind in ("normal", "ties", "flat"):
             for pol, p in _sel_policies(E, k, B):
-                cases.append(pytest.param(B, E, k, kind, pol, p, id=f"B{B}-E{E}-k{k}-{kind}-{pol}{p or ''}"))
+                tag = "-".join(map(str, p)) if isinstance(p, tuple) else (p or "")
+                cases.append(pytest.param(B, E, k, kind, pol, p, id=f"B{B}-E{E}-k{k}-{kind}-{pol}{tag}"))
     return cases
 
 
@@ -245,18 +262,21 @@ def test_select_matches_oracle(B, E, k, kind, policy, p):
     a = policy_args(policy, p)
     r = L.Routing(B, E, k)
     lg = to_dev(Lh, "f32")
-    L.moe_select(lg, L.make_policy(a["policy"], k, a["k0"], a["m"]), r)
+    L.moe_select(lg, L.make_policy(a["policy"], k, a["k0"], a["m"], a["g"]), r)
     torch.cuda.synchronize()
     g = routing_numpy(r)
-    ids, M = orc.select(Lh, a["policy"], k, a["k0"], a["m"])
+    ids, M = orc.select(Lh, a["policy"], k, a["k0"], a["m"], a["g"])
     o = {"ids": ids, "w": orc.gate_weights(Lh, ids)}
     o.update(orc.compact(ids, E))
     if M is not None:
         np.testing.assert_allclose(g["mass"], M, rtol=2e-6, atol=1e-12, err_msg="batch_mass")
-        # Ranked on the GPU's own masses, the oracle's budget step must agree
+        # Ranked on the GPU's own masses, the oracle's batch step must agree
         # exactly (masses that differ only by rounding may order differently).
-        ids_g = orc.select_budget(Lh, k, a["m"], mass=g["mass"])
-        assert np.array_equal(g["ids"], ids_g), "budget set ranked on the GPU masses"
+        if policy == "budget":
+            ids_g = orc.select_budget(Lh, k, a["m"], mass=g["mass"])
+        else:
+            ids_g = orc.select_hier(Lh, k, a["m"], a["k0"], a["g"], mass=g["mass"])
+        assert np.array_equal(g["ids"], ids_g), f"{policy} set ranked on the GPU masses"
     assert_routing_equal(g, o, f"B{B} E{E} k{k} {kind} {policy}{p}")
 
 
@@ -290,13 +310,15 @@ def _custom_layer(B, d, E, I, k, dtype="bf16", seed=0, bias=None, wg_scale=1.0):
     (256, 64, 256, 64, 16, "topk", 0, "bf16"),   # largest B, E and k
     (256, 64, 256, 64, 16, "oea", 3, "bf16"),
     (256, 64, 256, 64, 16, "budget", 40, "bf16"),
+    (256, 64, 256, 64, 16, "hier", (96, 20, 8), "bf16"),  # 32 requests of 8 tokens
+    (7, 136, 12, 40, 4, "hier", (9, 3, 3), "bf16"),      # ragged last request
     (9, 4096, 8, 64, 2, "topk", 0, "bf16"),      # deep reduction, several d slices
 ])
 def test_edge_layers(B, d, E, I, k, policy, p, dtype):
     cfg, inp, dev = _custom_layer(B, d, E, I, k, dtype)
     a = policy_args(policy, p)
-    Lg, rg, y = _run_layer(cfg, inp, dev, B, a["policy"], a["k0"], a["m"])
-    o = _oracle(cfg, inp, B, a["policy"], a["k0"], a["m"])
+    Lg, rg, y = _run_layer(cfg, inp, dev, B, a["policy"], a["k0"], a["m"], g=a["g"])
+    o = _oracle(cfg, inp, B, a["policy"], a["k0"], a["m"], g=a["g"])
     assert_logits_close(Lg, o["logits"])
     assert_routing_equal(rg, o, w_rtol=weight_rtol_from_logits(Lg, o["logits"]))
     assert_y_close(y_to_f64(y), o["y"], dtype)
