@@ -322,25 +322,35 @@ __device__ __forceinline__ void select_block(
 #pragma unroll
         for (int v = 0; v < NV; ++v) Mr[v] = 0.0f;
         const int t1 = min(B, r * g + g);
-        for (int t = r * g; t < t1; ++t) {
-          float lv[NV];
+        for (int t0 = r * g; t0 < t1; t0 += 4) {
+          // Four token rows per round trip (rows past the request are
+          // clamped loads, never used).
+          float lv[4][NV];
 #pragma unroll
-          for (int v = 0; v < NV; ++v)
-            lv[v] = __hip_atomic_load(const_cast<float *>(logits) + t * E + min(lane + 64 * v, E - 1),
-                                      __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          float mx = -INFINITY;
+          for (int q = 0; q < 4; ++q)
 #pragma unroll
-          for (int v = 0; v < NV; ++v)
-            if (lane + 64 * v < E) mx = fmaxf(mx, lv[v]);
-          mx = wave_maxf(mx);
-          float sm = 0.0f;
+            for (int v = 0; v < NV; ++v)
+              lv[q][v] = __hip_atomic_load(
+                  const_cast<float *>(logits) + min(t0 + q, t1 - 1) * E + min(lane + 64 * v, E - 1),
+                  __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 #pragma unroll
-          for (int v = 0; v < NV; ++v)
-            if (lane + 64 * v < E) sm += expf(lv[v] - mx);
-          sm = wave_sum(sm);
+          for (int q = 0; q < 4; ++q) {
+            if (t0 + q < t1) {  // wave-uniform; tokens in order
+              float mx = -INFINITY;
 #pragma unroll
-          for (int v = 0; v < NV; ++v)
-            if (lane + 64 * v < E) Mr[v] += expf(lv[v] - mx) / sm;
+              for (int v = 0; v < NV; ++v)
+                if (lane + 64 * v < E) mx = fmaxf(mx, lv[q][v]);
+              mx = wave_maxf(mx);
+              float sm = 0.0f;
+#pragma unroll
+              for (int v = 0; v < NV; ++v)
+                if (lane + 64 * v < E) sm += expf(lv[q][v] - mx);
+              sm = wave_sum(sm);
+#pragma unroll
+              for (int v = 0; v < NV; ++v)
+                if (lane + 64 * v < E) Mr[v] += expf(lv[q][v] - mx) / sm;
+            }
+          }
         }
         uint32_t key[NV];
 #pragma unroll
