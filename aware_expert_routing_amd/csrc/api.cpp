@@ -155,8 +155,9 @@ moe_status_t moe_layer_decode(const void *x, const void *w_g, const float *bias,
   hipStream_t s = static_cast<hipStream_t>(stream);
   char *ws = static_cast<char *>(workspace);
   if (dt == MOE_BF16) {
+    float *part = reinterpret_cast<float *>(ws + plan.router_part);
     uint32_t *cnt = reinterpret_cast<uint32_t *>(ws + kRouteSelectCntOffset);
-    MOE_TRY(hip_status(launch_route_select(x, w_g, bias, B, d, E, logits, cnt, policy, *routing, s)));
+    MOE_TRY(hip_status(launch_route_select(x, w_g, bias, B, d, E, logits, part, cnt, policy, *routing, s)));
   } else {
     float *part = reinterpret_cast<float *>(ws + plan.router_part);
     uint32_t *cnt = reinterpret_cast<uint32_t *>(ws + kRouterCntOffset);

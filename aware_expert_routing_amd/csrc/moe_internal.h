@@ -96,10 +96,10 @@ hipError_t launch_router(const void *x, const void *w_g, const float *bias, moe_
 hipError_t launch_select(const float *logits, int B, int E, moe_policy_t p,
                          const moe_routing_t &r, hipStream_t s);
 
-// bf16 router and selection in one launch; cnt is a counter word (zero before,
-// zero after).
+// bf16 router and selection in one launch; part holds the slices' partial
+// logit tiles, cnt is a counter word (zero before, zero after).
 hipError_t launch_route_select(const void *x, const void *w_g, const float *bias, int B, int d,
-                               int E, float *logits, uint32_t *cnt, moe_policy_t p,
+                               int E, float *logits, float *part, uint32_t *cnt, moe_policy_t p,
                                const moe_routing_t &r, hipStream_t s);
 
 // Read-only scan of `bytes` (a multiple of 16) at src by kReadStreamBlocks

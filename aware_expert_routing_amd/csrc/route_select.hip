@@ -1,10 +1,13 @@
 // Router and selection in one launch (bf16 layers, moe_layer_decode).
-// Each 1024-thread workgroup computes one 16 x 16 tile of the logits
-// (router_tile) and stores it with device-scope stores; it then counts itself
-// on a counter in the workspace. The workgroup that completes the count runs
-// the whole selection (select_block) on the finished logits and resets the
-// counter. The logits are bit-identical to moe_route's, and the routing to
-// moe_select's on them.
+// Grid (ceil(E/16), ceil(B/16), slices of 512 rows of d): each 1024-thread
+// workgroup computes the partial 16 x 16 logit tile of one slice
+// (router_partial), stores it with device-scope stores and counts itself on
+// a counter in the workspace. The workgroup that completes the count forms
+// every logit as bias + slice 0 + slice 1 + ... (router_logit, the same sum
+// in the same order as moe_route's), straight into the selection's registers,
+// writes the logits output, runs the whole selection (select_block) and
+// resets the counter. The logits are bit-identical to moe_route's, and the
+// routing to moe_select's on them.
 #include "router_impl.h"
 #include "select_impl.h"
 
@@ -13,39 +16,60 @@ namespace {
 
 static_assert(kRtThreads == kThreads, "router tile and selection share the workgroup size");
 
+// Logits completed from the slices' partial tiles; each value read is also
+// written to the logits output.
+struct SliceLogits {
+  const float *part;
+  const float *bias;
+  float *out;
+  int E, tiles_e, slices;
+  __device__ __forceinline__ float operator()(int t, int e) const {
+    return router_logit(part, bias, t, e, tiles_e, slices);
+  }
+  __device__ __forceinline__ void emit(int t, int e, float v) const { out[size_t(t) * E + e] = v; }
+};
+
 template <bool VEC, int NV, int TPW>
 __global__ __launch_bounds__(kThreads) void route_select_kernel(
     const uint16_t *__restrict__ x, const uint16_t *__restrict__ w, const float *__restrict__ bias,
-    int B, int d, int E, float *__restrict__ logits, uint32_t *__restrict__ cnt, int kind, int k,
-    int k0, int m, int g, int32_t *__restrict__ topk_ids, float *__restrict__ topk_w,
-    int32_t *__restrict__ n_active, int32_t *__restrict__ active_experts,
-    int32_t *__restrict__ expert_offsets, int32_t *__restrict__ pair_token,
-    int32_t *__restrict__ pair_slot, float *__restrict__ batch_mass) {
+    int B, int d, int E, float *__restrict__ logits, float *__restrict__ part,
+    uint32_t *__restrict__ cnt, int kind, int k, int k0, int m, int g,
+    int32_t *__restrict__ topk_ids, float *__restrict__ topk_w, int32_t *__restrict__ n_active,
+    int32_t *__restrict__ active_experts, int32_t *__restrict__ expert_offsets,
+    int32_t *__restrict__ pair_token, int32_t *__restrict__ pair_slot,
+    float *__restrict__ batch_mass) {
   __shared__ RouterLds sm;
   __shared__ int s_last;
-  router_tile<VEC>(x, w, bias, B, d, E, logits, sm);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this tile's logits are stored
+  const int slices = gridDim.z;
+  const int tile = blockIdx.x + gridDim.x * blockIdx.y;
+  const float v = router_partial<VEC>(x, w, B, d, E, blockIdx.z, sm);
+  if (threadIdx.x < kRtTile * kRtTile)
+    __hip_atomic_store(part + (size_t(tile) * slices + blockIdx.z) * (kRtTile * kRtTile) + threadIdx.x, v,
+                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this slice's partial tile is stored
   __syncthreads();
   if (threadIdx.x == 0) {
+    const uint32_t total = gridDim.x * gridDim.y * gridDim.z;
     const uint32_t before =
         __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    s_last = before == gridDim.x * gridDim.y - 1;
+    s_last = before == total - 1;
     if (s_last) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   __syncthreads();
   if (!s_last) return;
-  select_block<NV, TPW>(logits, B, E, kind, k, k0, m, g, topk_ids, topk_w, n_active, active_experts,
-                   expert_offsets, pair_token, pair_slot, batch_mass);
+  select_block<NV, TPW>(SliceLogits{part, bias, logits, E, int(gridDim.x), slices}, B, E, kind, k, k0,
+                        m, g, topk_ids, topk_w, n_active, active_experts, expert_offsets, pair_token,
+                        pair_slot, batch_mass);
 }
 
 template <bool VEC>
 void launch_rs(dim3 grid, const uint16_t *x, const uint16_t *w, const float *bias, int B, int d,
-               int E, float *logits, uint32_t *cnt, const moe_policy_t &p, const moe_routing_t &r,
-               hipStream_t s) {
+               int E, float *logits, float *part, uint32_t *cnt, const moe_policy_t &p,
+               const moe_routing_t &r, hipStream_t s) {
   float *mass = (p.kind == MOE_POLICY_BUDGET || p.kind == MOE_POLICY_HIER) ? r.batch_mass : nullptr;
   dispatch_select_shape(B, E, [&](auto nv, auto tpw) {
     route_select_kernel<VEC, decltype(nv)::value, decltype(tpw)::value><<<grid, kThreads, 0, s>>>(
-        x, w, bias, B, d, E, logits, cnt, p.kind, p.k, p.k0, p.m, p.g, r.topk_ids, r.topk_w,
+        x, w, bias, B, d, E, logits, part, cnt, p.kind, p.k, p.k0, p.m, p.g, r.topk_ids, r.topk_w,
         r.n_active, r.active_experts, r.expert_offsets, r.pair_token, r.pair_slot, mass);
   });
 }
@@ -53,14 +77,14 @@ void launch_rs(dim3 grid, const uint16_t *x, const uint16_t *w, const float *bia
 }  // namespace
 
 hipError_t launch_route_select(const void *x, const void *w_g, const float *bias, int B, int d,
-                               int E, float *logits, uint32_t *cnt, moe_policy_t p,
+                               int E, float *logits, float *part, uint32_t *cnt, moe_policy_t p,
                                const moe_routing_t &r, hipStream_t s) {
-  const dim3 grid(ceil_div(E, kRtTile), ceil_div(B, kRtTile));
+  const dim3 grid(ceil_div(E, kRtTile), ceil_div(B, kRtTile), router_slices(d));
   const uint16_t *xb = static_cast<const uint16_t *>(x), *wb = static_cast<const uint16_t *>(w_g);
   if (E % kRtTile == 0)
-    launch_rs<true>(grid, xb, wb, bias, B, d, E, logits, cnt, p, r, s);
+    launch_rs<true>(grid, xb, wb, bias, B, d, E, logits, part, cnt, p, r, s);
   else
-    launch_rs<false>(grid, xb, wb, bias, B, d, E, logits, cnt, p, r, s);
+    launch_rs<false>(grid, xb, wb, bias, B, d, E, logits, part, cnt, p, r, s);
   return hipGetLastError();
 }
 

@@ -3,7 +3,9 @@
 // Cost", step 1). W_g is [d, E], contiguous along E.
 //
 // bf16: one 1024-thread workgroup per 16-token x 16-expert tile of the
-// logits, over the whole reduction, on MFMA (router_tile in router_impl.h).
+// logits and slice of 512 rows of the reduction, on MFMA (router_partial in
+// router_impl.h); it stores the slice's partial tile, and the workgroup that
+// completes the tile's count adds the bias and the slices in order.
 //
 // float32 (small layers): a workgroup owns a 16-token x 16-expert tile of
 // the logits and one slice of kRouterRows rows of the reduction: it stages
@@ -59,13 +61,33 @@ __device__ __forceinline__ void stage(const T *__restrict__ src, size_t ld, int 
   }
 }
 
-// bf16: grid = (ceil(E/16), ceil(B/16)); block = 1024.
+// bf16: grid = (ceil(E/16), ceil(B/16), slices); block = 1024.
 template <bool VEC>
 __global__ __launch_bounds__(kRtThreads) void router_mfma_kernel(
     const uint16_t *__restrict__ x, const uint16_t *__restrict__ w, const float *__restrict__ bias,
-    int B, int d, int E, float *__restrict__ logits) {
+    int B, int d, int E, float *__restrict__ part, uint32_t *__restrict__ cnt,
+    float *__restrict__ logits) {
   __shared__ RouterLds sm;
-  router_tile<VEC>(x, w, bias, B, d, E, logits, sm);
+  __shared__ int s_last;
+  const int slices = gridDim.z;
+  const int tile = blockIdx.x + gridDim.x * blockIdx.y;
+  const float v = router_partial<VEC>(x, w, B, d, E, blockIdx.z, sm);
+  if (threadIdx.x < kRtTile * kRtTile)
+    __hip_atomic_store(part + (size_t(tile) * slices + blockIdx.z) * (kRtTile * kRtTile) + threadIdx.x, v,
+                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this slice's partial tile is stored
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const uint32_t before =
+        __hip_atomic_fetch_add(cnt + tile, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    s_last = before == uint32_t(slices - 1);
+    if (s_last) __hip_atomic_store(cnt + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __syncthreads();
+  if (!s_last || threadIdx.x >= kRtTile * kRtTile) return;
+  const int t = blockIdx.y * kRtTile + threadIdx.x / kRtTile;
+  const int e = blockIdx.x * kRtTile + threadIdx.x % kRtTile;
+  if (t < B && e < E) logits[size_t(t) * E + e] = router_logit(part, bias, t, e, gridDim.x, slices);
 }
 
 // float32: grid = (ceil(E/16), slices, ceil(B/16)); block = 256 = 16 x 16
@@ -119,12 +141,12 @@ __global__ __launch_bounds__(kThreads) void router_kernel(
 hipError_t launch_router(const void *x, const void *w_g, const float *bias, moe_dtype_t dt, int B,
                          int d, int E, float *part, uint32_t *cnt, float *logits, hipStream_t s) {
   if (dt == MOE_BF16) {
-    const dim3 grid(ceil_div(E, kTile), ceil_div(B, kTile));
+    const dim3 grid(ceil_div(E, kTile), ceil_div(B, kTile), router_slices(d));
     const uint16_t *xb = static_cast<const uint16_t *>(x), *wb = static_cast<const uint16_t *>(w_g);
     if (E % kTile == 0)
-      router_mfma_kernel<true><<<grid, kRtThreads, 0, s>>>(xb, wb, bias, B, d, E, logits);
+      router_mfma_kernel<true><<<grid, kRtThreads, 0, s>>>(xb, wb, bias, B, d, E, part, cnt, logits);
     else
-      router_mfma_kernel<false><<<grid, kRtThreads, 0, s>>>(xb, wb, bias, B, d, E, logits);
+      router_mfma_kernel<false><<<grid, kRtThreads, 0, s>>>(xb, wb, bias, B, d, E, part, cnt, logits);
     return hipGetLastError();
   }
   dim3 grid(ceil_div(E, kTile), ceil_div(d, kRouterRows), ceil_div(B, kTile));

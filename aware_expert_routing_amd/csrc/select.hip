@@ -12,7 +12,7 @@ __global__ __launch_bounds__(kThreads) void select_kernel(
     int32_t *__restrict__ active_experts, int32_t *__restrict__ expert_offsets,
     int32_t *__restrict__ pair_token, int32_t *__restrict__ pair_slot,
     float *__restrict__ batch_mass) {
-  select_block<NV, TPW>(logits, B, E, kind, k, k0, m, g, topk_ids, topk_w, n_active, active_experts,
+  select_block<NV, TPW>(StoredLogits{logits, E}, B, E, kind, k, k0, m, g, topk_ids, topk_w, n_active, active_experts,
                    expert_offsets, pair_token, pair_slot, batch_mass);
 }
 

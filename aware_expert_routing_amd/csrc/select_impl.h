@@ -178,13 +178,25 @@ __device__ __forceinline__ int wave_rank(uint32_t (&key)[NV], int rounds, int ba
 
 __device__ __forceinline__ bool bit_of(const uint32_t *mask, int e) { return (mask[e >> 5] >> (e & 31)) & 1u; }
 
-// The whole selection, run by one workgroup of kThreads threads. The logits
-// are read with device-scope loads, so they may come from other workgroups
-// of the same kernel. TPW token slots per wave (B <= 16 * TPW): the per-token
+// Source of the float32 logits: logit(t, e) with 0 <= t < B, 0 <= e < E,
+// and emit(t, e, v), called once for every (t, e) with the value read.
+// Logits stored in memory: device-scope loads (another workgroup of the same
+// kernel may have stored them); nothing to emit.
+struct StoredLogits {
+  const float *p;
+  int E;
+  __device__ __forceinline__ float operator()(int t, int e) const {
+    return __hip_atomic_load(const_cast<float *>(p) + t * E + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __device__ __forceinline__ void emit(int, int, float) const {}
+};
+
+// The whole selection, run by one workgroup of kThreads threads, on the
+// logits of `src`. TPW token slots per wave (B <= 16 * TPW): the per-token
 // phases are unrolled over the slots, so a small TPW keeps the code small.
-template <int NV, int TPW>
+template <int NV, int TPW, class Src>
 __device__ __forceinline__ void select_block(
-    const float *__restrict__ logits, int B, int E, int kind, int k, int k0, int m, int g,
+    const Src &src, int B, int E, int kind, int k, int k0, int m, int g,
     int32_t *__restrict__ topk_ids, float *__restrict__ topk_w, int32_t *__restrict__ n_active,
     int32_t *__restrict__ active_experts, int32_t *__restrict__ expert_offsets,
     int32_t *__restrict__ pair_token, int32_t *__restrict__ pair_slot,
@@ -223,17 +235,20 @@ __device__ __forceinline__ void select_block(
   if (kind == MOE_POLICY_HIER)
     for (int i = tid; i < ((B + g - 1) / g) * kWords; i += kThreads) req_allowed[i / kWords][i % kWords] = 0;
 
-  // Phase 1: logits into registers. Addresses are clamped so that every load
+  // Phase 1: logits into registers. Indices are clamped so that every read
   // is in bounds; values outside [B, E) are never used as candidates.
   float L[TPW][NV];
 #pragma unroll
   for (int ti = 0; ti < TPW; ++ti) {
     if (ti * kWaves < B) {  // wave-uniform
-      const int t = min(wave + kWaves * ti, B - 1);
+      const int tr = wave + kWaves * ti;
+      const int t = min(tr, B - 1);
 #pragma unroll
-      for (int v = 0; v < NV; ++v)
-        L[ti][v] = __hip_atomic_load(const_cast<float *>(logits) + t * E + min(lane + 64 * v, E - 1),
-                                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      for (int v = 0; v < NV; ++v) {
+        const int er = lane + 64 * v;
+        L[ti][v] = src(t, min(er, E - 1));
+        if (tr < B && er < E) src.emit(t, er, L[ti][v]);
+      }
     }
   }
   __syncthreads();
@@ -330,9 +345,7 @@ __device__ __forceinline__ void select_block(
           for (int q = 0; q < 4; ++q)
 #pragma unroll
             for (int v = 0; v < NV; ++v)
-              lv[q][v] = __hip_atomic_load(
-                  const_cast<float *>(logits) + min(t0 + q, t1 - 1) * E + min(lane + 64 * v, E - 1),
-                  __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+              lv[q][v] = src(min(t0 + q, t1 - 1), min(lane + 64 * v, E - 1));
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
             if (t0 + q < t1) {  // wave-uniform; tokens in order
