@@ -24,9 +24,10 @@
 //     v_mfma_f32_16x16x32_bf16, up to 64 tokens per pass.
 //   * Gate/up slice partial sums go to the workspace; after a grid barrier
 //     the grid forms h = SiLU(g) * u; after a second one the down items run.
-//   * A down pass counts its tokens on per-(token, strip) counters; the
-//     workgroup that completes a token's count forms y for that strip, adding
-//     the slots in order (no float atomics: results are reproducible).
+//   * A down pass adds its tokens to per-(16-token group, strip) counters;
+//     the workgroup that completes a group's count forms y over that strip
+//     for the group's tokens, adding the slots in order (no float atomics:
+//     results are reproducible).
 // float32 path (small layers): plain dot products, 16 row groups per column.
 #include "moe_internal.h"
 
@@ -53,16 +54,17 @@ static_assert(kStripCols == 64 && kBK == 128, "tile constants");
 // Routing lists staged in LDS once per workgroup (the loop reads them with
 // the inline-assembly helpers below). Every field is aligned to its element
 // size (LDS atomics need natural alignment) and the area to 16 bytes.
-constexpr int kMetaLast = 0;                            // int32 tokens whose strip this pass completes
+constexpr int kMetaLast = 0;                            // int32 token groups whose strip this pass completes
 constexpr int kMetaNLast = kMetaLast + 4 * kMaxTok;     // int32 their number
 constexpr int kMetaFill = kMetaNLast + 16;              // uint32 filled slots of each token
 constexpr int kMetaRow = kMetaFill + 4 * kMaxB;         // int16 token slot t*k+j of each pair
 constexpr int kMetaAct = kMetaRow + 2 * kMaxPairs;      // int16 active expert list
 constexpr int kMetaOff = kMetaAct + 2 * kMaxE;          // int16 CSR offsets
-constexpr int kMetaTok = kMetaOff + 2 * (kMaxE + 1);    // uint8 token of each pair
+constexpr int kMetaGFill = kMetaOff + 2 * (kMaxE + 1) + 2;  // uint32 filled slots of each token group
+constexpr int kMetaTok = kMetaGFill + 4 * kTokGroups;   // uint8 token of each pair
 constexpr int kMetaBytes = (kMetaTok + kMaxPairs + 15) / 16 * 16;
 static_assert(kMetaNLast % 4 == 0 && kMetaFill % 4 == 0 && kMetaRow % 2 == 0 && kMetaAct % 2 == 0 &&
-                  kMetaOff % 2 == 0,
+                  kMetaOff % 2 == 0 && kMetaGFill % 4 == 0,
               "meta field alignment");
 
 // LDS plan of one instantiation. A stage slot holds NMAT weight tiles
@@ -295,7 +297,7 @@ struct Params {
   const int32_t *pair_token;  // [P]
   const int32_t *pair_slot;   // [P]
   uint32_t *sync;             // grid-barrier words
-  uint32_t *tok_cnt;          // [B][n_dstrips] down passes counted per (token, strip)
+  uint32_t *grp_cnt;          // per (strip, token group): slots counted, one 128-byte line each
   int n_dstrips;              // 128-column strips of d
 };
 
@@ -607,76 +609,120 @@ __device__ __forceinline__ void barrier_no_wait() {
   asm volatile("" ::: "memory");
 }
 
-// End of a down pass (its rows stored by every wave). Each token of the pass
-// is counted on its (token, strip) counter; the workgroup that brings the
-// count to the token's number of filled slots forms y[t] over the strip,
-// adding w[t,j] * part[t*k+j] in slot order (empty slots skipped), and resets
-// the counter. A count is taken only after this workgroup's stores have
-// completed, so the last one finds every row of the token in place.
+// Counter of (token group grp, down strip) on a 128-byte line of its own.
+__device__ __forceinline__ uint32_t *group_counter(const Params &p, int grp, int strip) {
+  return p.grp_cnt + (size_t(strip) * kTokGroups + grp) * kCntStride;
+}
+
+// y over 128-column strip `strip` for the tokens of group grp: thread i takes
+// token 16*grp + i/16 and columns 8*(i%16) .. +7 of the strip, adding
+// w[t,j] * part[t*k+j] in slot order (empty slots skipped). Slots are taken
+// eight at a time with every load of a round issued before the first use.
+static_assert(kThreads == kTokGroup * (2 * kStripCols / 8), "one thread per token and 8 columns");
+__device__ __forceinline__ void combine_group(const Params &p, int grp, int strip) {
+  const int t = grp * kTokGroup + (threadIdx.x >> 4);
+  const int col = strip * 2 * kStripCols + (threadIdx.x & 15) * 8;
+  if (t >= p.B || col >= p.d) return;
+  const __amdgpu_buffer_rsrc_t rp = make_rsrc(p.part, uint32_t(p.P) * uint32_t(p.d) * 4u);
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int j0 = 0; j0 < p.k; j0 += 8) {
+    int id[8];
+    float w[8];
+    float4 v[8][2];
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj) {
+      const int j = j0 + jj;
+      if (j < p.k) {
+        const int slot = t * p.k + j;
+        id[jj] = p.ids[slot];
+        w[jj] = p.w[slot];
+        const uint32_t off = (uint32_t(slot) * uint32_t(p.d) + uint32_t(col)) * 4u;
+        v[jj][0] = ld_dev4(rp, off);
+        v[jj][1] = ld_dev4(rp, off + 16u);
+      }
+    }
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj) {
+      if (j0 + jj < p.k && id[jj] >= 0) {
+        acc[0] = fmaf(w[jj], v[jj][0].x, acc[0]);
+        acc[1] = fmaf(w[jj], v[jj][0].y, acc[1]);
+        acc[2] = fmaf(w[jj], v[jj][0].z, acc[2]);
+        acc[3] = fmaf(w[jj], v[jj][0].w, acc[3]);
+        acc[4] = fmaf(w[jj], v[jj][1].x, acc[4]);
+        acc[5] = fmaf(w[jj], v[jj][1].y, acc[5]);
+        acc[6] = fmaf(w[jj], v[jj][1].z, acc[6]);
+        acc[7] = fmaf(w[jj], v[jj][1].w, acc[7]);
+      }
+    }
+  }
+  uint4 o;
+  o.x = uint32_t(f32_to_bf16(acc[0])) | (uint32_t(f32_to_bf16(acc[1])) << 16);
+  o.y = uint32_t(f32_to_bf16(acc[2])) | (uint32_t(f32_to_bf16(acc[3])) << 16);
+  o.z = uint32_t(f32_to_bf16(acc[4])) | (uint32_t(f32_to_bf16(acc[5])) << 16);
+  o.w = uint32_t(f32_to_bf16(acc[6])) | (uint32_t(f32_to_bf16(acc[7])) << 16);
+  *reinterpret_cast<uint4 *>(p.y + size_t(t) * p.d + col) = o;
+}
+
+// End of a down pass (its rows stored by every wave). The pass adds, for
+// each 16-token group it has tokens of, their number to the group's counter
+// for the strip (one atomic per group, not per token: the atomics of one
+// counter are served in turn). The workgroup that brings a counter to the
+// group's number of filled slots forms y over the strip for the whole group
+// (combine_group) and resets the counter. A count is taken only after this
+// workgroup's stores have completed, so the last one finds every row of the
+// group in place.
 __device__ __forceinline__ void finish_down(const Cursor &c, const Params &p, unsigned char *meta,
                                             int wave, int lane) {
   const int T = min(kMaxTok, c.T - c.pass * kMaxTok);
   const int pbase = c.p0 + c.pass * kMaxTok;
   int32_t *last = reinterpret_cast<int32_t *>(meta + kMetaLast);
   int32_t *n_last = reinterpret_cast<int32_t *>(meta + kMetaNLast);
+  const uint32_t *gfill = reinterpret_cast<const uint32_t *>(meta + kMetaGFill);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   if (wave == 0) {
+    // The first lane of each run of lanes in one group adds the run's
+    // length (an expert's tokens ascend, so a group is one run).
+    const int grp = lane < T ? int(meta[kMetaTok + pbase + lane]) / kTokGroup : -1;
+    const int prev = __shfl_up(grp, 1);
+    const bool first = lane < T && (lane == 0 || prev != grp);
+    const unsigned long long fb = __ballot(first);
     bool mine = false;
-    int t = 0;
-    if (lane < T) {
-      t = meta[kMetaTok + pbase + lane];
-      const int filled = reinterpret_cast<const uint32_t *>(meta + kMetaFill)[t];
-      const uint32_t before = __hip_atomic_fetch_add(p.tok_cnt + t * p.n_dstrips + c.strip, 1u,
+    if (first) {
+      const unsigned long long above = lane == 63 ? 0ull : (fb >> (lane + 1));
+      const int run = above ? __builtin_ctzll(above) + 1 : T - lane;
+      const uint32_t before = __hip_atomic_fetch_add(group_counter(p, grp, c.strip), uint32_t(run),
                                                      __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      mine = before == uint32_t(filled - 1);
+      mine = before + uint32_t(run) == gfill[grp];
     }
     const unsigned long long b = __ballot(mine);
-    if (mine) last[__builtin_amdgcn_mbcnt_hi(uint32_t(b >> 32), __builtin_amdgcn_mbcnt_lo(uint32_t(b), 0))] = t;
+    if (mine) last[__builtin_amdgcn_mbcnt_hi(uint32_t(b >> 32), __builtin_amdgcn_mbcnt_lo(uint32_t(b), 0))] = grp;
     if (lane == 0) *n_last = __popcll(b);
   }
   __syncthreads();
   const int n = *n_last;
-  const __amdgpu_buffer_rsrc_t rp = make_rsrc(p.part, uint32_t(p.P) * uint32_t(p.d) * 4u);
-  constexpr int kGroups = 2 * kStripCols / 4;  // 4-column groups of a strip
-  for (int i = threadIdx.x; i < n * kGroups; i += kThreads) {
-    const int t = last[i / kGroups];
-    const int col = c.strip * 2 * kStripCols + (i % kGroups) * 4;
-    if (col < p.d) {
-      int id[kMaxK];
-      float w[kMaxK];
-      float4 v[kMaxK];
-#pragma unroll
-      for (int j = 0; j < kMaxK; ++j) {
-        if (j < p.k) {
-          const int slot = t * p.k + j;
-          id[j] = p.ids[slot];
-          w[j] = p.w[slot];
-          v[j] = ld_dev4(rp, (uint32_t(slot) * uint32_t(p.d) + uint32_t(col)) * 4u);
-        }
-      }
-      float4 acc = make_float4(0, 0, 0, 0);
-#pragma unroll
-      for (int j = 0; j < kMaxK; ++j) {
-        if (j < p.k && id[j] >= 0) {
-          acc.x = fmaf(w[j], v[j].x, acc.x);
-          acc.y = fmaf(w[j], v[j].y, acc.y);
-          acc.z = fmaf(w[j], v[j].z, acc.z);
-          acc.w = fmaf(w[j], v[j].w, acc.w);
-        }
-      }
-      ushort4 o;
-      o.x = f32_to_bf16(acc.x);
-      o.y = f32_to_bf16(acc.y);
-      o.z = f32_to_bf16(acc.z);
-      o.w = f32_to_bf16(acc.w);
-      *reinterpret_cast<ushort4 *>(p.y + size_t(t) * p.d + col) = o;
-    }
-    if (i % kGroups == 0)
-      __hip_atomic_store(p.tok_cnt + t * p.n_dstrips + c.strip, 0u, __ATOMIC_RELAXED,
-                         __HIP_MEMORY_SCOPE_AGENT);
+  for (int q = 0; q < n; ++q) {
+    const int grp = last[q];
+    combine_group(p, grp, c.strip);
+    if (threadIdx.x == 0)
+      __hip_atomic_store(group_counter(p, grp, c.strip), 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   __syncthreads();
+}
+
+// y over the strips of token groups that have no filled slot at all (no
+// down pass counts them): zero, written by workgroups b, b+G, ... of the
+// (group, strip) units. Such groups only come from caller-made routings.
+__device__ __forceinline__ void zero_empty_groups(const Params &p, const unsigned char *meta) {
+  const uint32_t *gfill = reinterpret_cast<const uint32_t *>(meta + kMetaGFill);
+  const int ngroups = (p.B + kTokGroup - 1) / kTokGroup;
+  for (int u = blockIdx.x; u < ngroups * p.n_dstrips; u += gridDim.x) {
+    const int grp = u / p.n_dstrips, strip = u - grp * p.n_dstrips;
+    if (gfill[grp] != 0) continue;
+    const int t = grp * kTokGroup + (threadIdx.x >> 4);
+    const int col = strip * 2 * kStripCols + (threadIdx.x & 15) * 8;
+    if (t < p.B && col < p.d) *reinterpret_cast<uint4 *>(p.y + size_t(t) * p.d + col) = make_uint4(0, 0, 0, 0);
+  }
 }
 
 // The change from gate/up to down in a workgroup: every gate/up stage of it
@@ -767,6 +813,14 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_kernel(Params p,
   // Filled slots of each token = its pairs in the list.
   for (int i = threadIdx.x; i < total; i += kThreads) atomicAdd(fill + meta[kMetaTok + i], 1u);
   __syncthreads();
+  // Filled slots of each 16-token group: the count that completes it.
+  if (threadIdx.x < kTokGroups) {
+    uint32_t gs = 0;
+    for (int t = threadIdx.x * kTokGroup; t < min(p.B, (threadIdx.x + 1) * kTokGroup); ++t) gs += fill[t];
+    reinterpret_cast<uint32_t *>(meta + kMetaGFill)[threadIdx.x] = gs;
+  }
+  __syncthreads();
+  zero_empty_groups(p, meta);
 
   // Whole-d gate/up tiles when the active experts' tiles (expert x 64-column
   // strip of I) fill enough of the grid to keep HBM busy: each tile then
@@ -988,7 +1042,7 @@ hipError_t launch_expert_ffn(const void *x, const void *w_gate, const void *w_up
     p.pair_token = r.pair_token;
     p.pair_slot = r.pair_slot;
     p.sync = reinterpret_cast<uint32_t *>(ws);
-    p.tok_cnt = reinterpret_cast<uint32_t *>(ws + kTokCntOffset);
+    p.grp_cnt = reinterpret_cast<uint32_t *>(ws + kGrpCntOffset);
     p.n_dstrips = ceil_div(d, 2 * kStripCols);
     // One workgroup per CU at most, so that the whole grid is resident and
     // the grid barriers cannot wait on a workgroup that has not started.

@@ -35,14 +35,20 @@ inline size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 // (the same for every size of call, so that calls of different sizes may
 // share a workspace): the expert FFN's grid-barrier words (first 384 bytes),
 // the fused router + selection counter, the router's per-tile counters (up
-// to 256 tiles) and the FFN's per-(token, 128-column strip) counters. All are
-// zero before the workspace's first use. Every call leaves the counters at
-// zero; the barrier's release word only grows. No other step writes them.
+// to 256 tiles) and the FFN's per-(16-token group, 128-column strip of d)
+// counters, each of those on a 128-byte line of its own (atomics on one line
+// are served one after another). All are zero before the workspace's first
+// use. Every call leaves the counters at zero; the barrier's release word
+// only grows. No other step writes them.
 constexpr size_t kSyncBytes = 2048;
 constexpr size_t kRouteSelectCntOffset = 384;  // fused router + selection: tiles done
 constexpr size_t kRouterCntOffset = 512;
-constexpr size_t kTokCntOffset = kSyncBytes;  // uint32 [kMaxB][kMaxDim / 128]
-constexpr size_t kCounterBytes = kTokCntOffset + size_t(kMaxB) * (kMaxDim / (2 * kStripCols)) * 4;
+constexpr int kTokGroup = 16;                      // tokens per combine group
+constexpr int kTokGroups = kMaxB / kTokGroup;      // groups at B = kMaxB
+constexpr int kCntStride = 32;                     // uint32 words between group counters
+constexpr size_t kGrpCntOffset = kSyncBytes;       // [kMaxDim / 128 strips][kTokGroups] x 128 B
+constexpr size_t kCounterBytes =
+    kGrpCntOffset + size_t(kMaxDim / (2 * kStripCols)) * kTokGroups * kCntStride * 4;
 
 // Workspace carve-up. Every segment starts on a 256-byte boundary.
 struct Workspace {
