@@ -80,37 +80,29 @@ __device__ __forceinline__ uint32_t dpp(uint32_t old, uint32_t v) {
   return uint32_t(__builtin_amdgcn_update_dpp(int(old), int(v), CTRL, ROWS, 0xF, false));
 }
 
-template <int CTRL, int ROWS>
-__device__ __forceinline__ uint32_t umax_step(uint32_t v) {
-  const uint32_t w = dpp<CTRL, ROWS>(v, v);
-  return w > v ? w : v;
-}
+// The same six steps with the lane move folded into the arithmetic (one
+// v_max_u32_dpp / v_add_f32_dpp per step: dst = op(moved v, v); rows that a
+// step does not write keep v). Two wait states precede every step, since each
+// reads through DPP the register the previous instruction wrote.
+#define MOE_DPP_STEPS(OP)                                                        \
+  "s_nop 1\n" OP " %0, %0, %0 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n" \
+  "s_nop 1\n" OP " %0, %0, %0 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf\n" \
+  "s_nop 1\n" OP " %0, %0, %0 row_half_mirror row_mask:0xf bank_mask:0xf\n"     \
+  "s_nop 1\n" OP " %0, %0, %0 row_mirror row_mask:0xf bank_mask:0xf\n"          \
+  "s_nop 1\n" OP " %0, %0, %0 row_bcast:15 row_mask:0xa bank_mask:0xf\n"        \
+  "s_nop 1\n" OP " %0, %0, %0 row_bcast:31 row_mask:0xc bank_mask:0xf\n"        \
+  "s_nop 1\n"
 
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
-  v = umax_step<kDppQuadX1, 0xF>(v);
-  v = umax_step<kDppQuadX2, 0xF>(v);
-  v = umax_step<kDppHalfMirror, 0xF>(v);
-  v = umax_step<kDppMirror, 0xF>(v);
-  v = umax_step<kDppBcast15, 0xA>(v);
-  v = umax_step<kDppBcast31, 0xC>(v);
+  asm volatile(MOE_DPP_STEPS("v_max_u32_dpp") : "+v"(v));
   return __builtin_amdgcn_readlane(v, 63);
 }
 
 // Sum over the wave in a fixed tree; every lane gets the lane-63 result, so
-// the value is uniform and reproducible from run to run.
-template <int CTRL, int ROWS>
-__device__ __forceinline__ float add_step(float v) {
-  // Lanes outside ROWS receive 0 (old) and keep their value.
-  return v + __uint_as_float(dpp<CTRL, ROWS>(0u, __float_as_uint(v)));
-}
-
+// the value is uniform and reproducible from run to run. (Lane 63 takes part
+// in every step, so rows left out of a step do not affect it.)
 __device__ __forceinline__ float wave_sum(float v) {
-  v = add_step<kDppQuadX1, 0xF>(v);
-  v = add_step<kDppQuadX2, 0xF>(v);
-  v = add_step<kDppHalfMirror, 0xF>(v);
-  v = add_step<kDppMirror, 0xF>(v);
-  v = add_step<kDppBcast15, 0xA>(v);
-  v = add_step<kDppBcast31, 0xC>(v);
+  asm volatile(MOE_DPP_STEPS("v_add_f32_dpp") : "+v"(v));
   return __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(v), 63));
 }
 
