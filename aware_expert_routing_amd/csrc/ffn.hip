@@ -107,6 +107,10 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, ui
 // scope (across XCDs), which data exchanged between workgroups of one kernel
 // needs.
 constexpr int kPolicyDevice = 16;
+// NT marks a copy as streaming (read once): the expert weights are copied
+// with it, which was measured to shorten every stage of the kernel (the
+// weights then do not displace reused lines in the caches).
+constexpr int kPolicyStream = 2;
 
 // Copies 16 bytes per lane from buffer offset voff + soff into LDS at
 // dst + 16*lane. Offsets at or past the end of the buffer read as zero.
@@ -173,58 +177,6 @@ __device__ __forceinline__ int lds_i16(uint32_t a) {
   int v;
   asm volatile("ds_read_i16 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=&v"(v) : "v"(a));
   return v;
-}
-
-__device__ __forceinline__ void lds_tr2(uint32_t a0, uint32_t a1, bf16x8_t &b) {
-  long lo, hi;
-  asm volatile("ds_read_b64_tr_b16 %0, %2\n\t"
-               "ds_read_b64_tr_b16 %1, %3\n\t"
-               "s_waitcnt lgkmcnt(0)"
-               : "=&v"(lo), "=&v"(hi)
-               : "v"(a0), "v"(a1));
-  __builtin_memcpy(&b, &lo, 8);
-  __builtin_memcpy(reinterpret_cast<char *>(&b) + 8, &hi, 8);
-}
-
-__device__ __forceinline__ void lds_tr4(uint32_t a0, uint32_t a1, uint32_t a2, uint32_t a3,
-                                        bf16x8_t &b0, bf16x8_t &b1) {
-  long v0, v1, v2, v3;
-  asm volatile("ds_read_b64_tr_b16 %0, %4\n\t"
-               "ds_read_b64_tr_b16 %1, %5\n\t"
-               "ds_read_b64_tr_b16 %2, %6\n\t"
-               "ds_read_b64_tr_b16 %3, %7\n\t"
-               "s_waitcnt lgkmcnt(0)"
-               : "=&v"(v0), "=&v"(v1), "=&v"(v2), "=&v"(v3)
-               : "v"(a0), "v"(a1), "v"(a2), "v"(a3));
-  __builtin_memcpy(&b0, &v0, 8);
-  __builtin_memcpy(reinterpret_cast<char *>(&b0) + 8, &v1, 8);
-  __builtin_memcpy(&b1, &v2, 8);
-  __builtin_memcpy(reinterpret_cast<char *>(&b1) + 8, &v3, 8);
-}
-
-template <int NA>
-__device__ __forceinline__ void lds_b128(const uint32_t (&a)[4], bf16x8_t (&x)[4]);
-template <>
-__device__ __forceinline__ void lds_b128<1>(const uint32_t (&a)[4], bf16x8_t (&x)[4]) {
-  asm volatile("ds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=&v"(x[0]) : "v"(a[0]));
-}
-template <>
-__device__ __forceinline__ void lds_b128<2>(const uint32_t (&a)[4], bf16x8_t (&x)[4]) {
-  asm volatile("ds_read_b128 %0, %2\n\tds_read_b128 %1, %3\n\ts_waitcnt lgkmcnt(0)"
-               : "=&v"(x[0]), "=&v"(x[1]) : "v"(a[0]), "v"(a[1]));
-}
-template <>
-__device__ __forceinline__ void lds_b128<3>(const uint32_t (&a)[4], bf16x8_t (&x)[4]) {
-  asm volatile("ds_read_b128 %0, %3\n\tds_read_b128 %1, %4\n\tds_read_b128 %2, %5\n\t"
-               "s_waitcnt lgkmcnt(0)"
-               : "=&v"(x[0]), "=&v"(x[1]), "=&v"(x[2]) : "v"(a[0]), "v"(a[1]), "v"(a[2]));
-}
-template <>
-__device__ __forceinline__ void lds_b128<4>(const uint32_t (&a)[4], bf16x8_t (&x)[4]) {
-  asm volatile("ds_read_b128 %0, %4\n\tds_read_b128 %1, %5\n\tds_read_b128 %2, %6\n\t"
-               "ds_read_b128 %3, %7\n\ts_waitcnt lgkmcnt(0)"
-               : "=&v"(x[0]), "=&v"(x[1]), "=&v"(x[2]), "=&v"(x[3])
-               : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]));
 }
 
 // Grid-barrier words in the workspace, each on its own 128-byte line: the
@@ -423,36 +375,37 @@ struct Stream {
       for (int h = 0; h < 4; ++h) {
         const int rr = 8 * (vw + 4 * h) + (lane >> 3);
         const uint32_t voff = uint32_t(rr) * uint32_t(p.d) * 2u + uint32_t((lane & 7) ^ swz_w(rr)) * 16u;
-        dma16(r, slot + mat * kWTile + (vw + 4 * h) * 1024, voff, soff);
+        dma16<kPolicyStream>(r, slot + mat * kWTile + (vw + 4 * h) * 1024, voff, soff);
       }
     }
   }
 
-  // Issues every copy of stage c into `slot` (S::kCopies per wave).
-  __device__ __forceinline__ void issue(const Cursor &c, unsigned char *slot) const {
+  // Issues half of this wave's copies of stage c into `slot`: half 0 the
+  // first weight tile and the A tile, half 1 the second weight tile
+  // (S::kCopies per wave in all).
+  __device__ __forceinline__ void issue_half(const Cursor &c, unsigned char *slot, int half) const {
     if (c.up) {
       const size_t base = (size_t(c.e) * p.d + c.row0) * p.I;
       const uint32_t wbytes = uint32_t(c.nrows) * uint32_t(p.I) * 2u;
       const uint32_t soff =
           (uint32_t(c.kst * kBK) * uint32_t(p.I) + uint32_t(c.strip * kStripCols)) * 2u;
+      const __amdgpu_buffer_rsrc_t r = make_rsrc(p.W[half] + base, wbytes);
 #pragma unroll
-      for (int mat = 0; mat < 2; ++mat) {
-        const __amdgpu_buffer_rsrc_t r = make_rsrc(p.W[mat] + base, wbytes);
-#pragma unroll
-        for (int h = 0; h < 4; ++h) dma16(r, slot + mat * kWTile + (wave + 4 * h) * 1024, wv_up[h], soff);
-      }
+      for (int h = 0; h < 4; ++h) dma16<kPolicyStream>(r, slot + half * kWTile + (wave + 4 * h) * 1024, wv_up[h], soff);
     } else {
       const size_t base = size_t(c.e) * p.I * p.d;
       const __amdgpu_buffer_rsrc_t r = make_rsrc(p.W[2] + base, uint32_t(p.I) * uint32_t(p.d) * 2u);
+      const uint32_t soff = (uint32_t(c.kst * kBK) * uint32_t(p.d) +
+                             uint32_t((2 * c.strip + half) * kStripCols)) * 2u;
 #pragma unroll
-      for (int mat = 0; mat < 2; ++mat) {
-        const uint32_t soff = (uint32_t(c.kst * kBK) * uint32_t(p.d) +
-                               uint32_t((2 * c.strip + mat) * kStripCols)) * 2u;
-#pragma unroll
-        for (int h = 0; h < 4; ++h) dma16(r, slot + mat * kWTile + (wave + 4 * h) * 1024, wv_dn[h], soff);
-      }
+      for (int h = 0; h < 4; ++h) dma16<kPolicyStream>(r, slot + half * kWTile + (wave + 4 * h) * 1024, wv_dn[h], soff);
     }
-    issue_a(c, slot);
+    if (half == 0) issue_a(c, slot);
+  }
+  // Issues every copy of stage c into `slot`.
+  __device__ __forceinline__ void issue(const Cursor &c, unsigned char *slot) const {
+    issue_half(c, slot, 0);
+    issue_half(c, slot, 1);
   }
 };
 
@@ -468,45 +421,143 @@ __device__ __forceinline__ void clear(Acc &acc) {
   }
 }
 
-// B fragments of k-step ks for this lane: column 16*wave + j, rows
-// 32ks + 8g .. 32ks + 8g + 7 of both weight tiles. The transposing read gives
-// lane j of a 16-lane group element j of the four rows its group's lanes point
-// at (lane 4r+q points at row r, columns 4q..4q+3).
-__device__ __forceinline__ void b_frags(uint32_t slot, const uint32_t (&trc)[2], int ks,
-                                        bf16x8_t (&b)[2]) {
-  const uint32_t o = slot + uint32_t(ks * 32 * kRowBytes);
-  lds_tr4(o + trc[0], o + trc[1], o + kWTile + trc[0], o + kWTile + trc[1], b[0], b[1]);
-}
+// Operand fragments of k-steps 2*KP and 2*KP+1 of a stage, read from LDS by
+// one inline-assembly block that waits once, so that the reads of two
+// k-steps overlap. Per k-step ks:
+//   B fragments (column 16*wave + j, rows 32ks + 8g .. +7 of both weight
+//   tiles): four transposing reads at the lane's offsets b0 and b1 (rows
+//   8g + 4h + j/4 of the k-step), in tile 0 and in tile 1 (kWTile further);
+//   the read gives lane j of a 16-lane group element j of the four rows its
+//   group's lanes point at (lane 4r+q points at row r, columns 4q..4q+3);
+//   A fragments: NA reads of 16 bytes at xa[mt] + ks * XS (row tile mt).
+#define MOE_TR_PAIR(J)                                                   \
+  "ds_read_b64_tr_b16 %[t" #J "0], %[B0] offset:%[ob" #J "]\n\t"         \
+  "ds_read_b64_tr_b16 %[t" #J "1], %[B1] offset:%[ob" #J "]\n\t"         \
+  "ds_read_b64_tr_b16 %[t" #J "2], %[B0] offset:%[ow" #J "]\n\t"         \
+  "ds_read_b64_tr_b16 %[t" #J "3], %[B1] offset:%[ow" #J "]\n\t"
+#define MOE_TR_OUTS                                                            \
+  [t00] "=&v"(t[0][0]), [t01] "=&v"(t[0][1]), [t02] "=&v"(t[0][2]), [t03] "=&v"(t[0][3]), \
+  [t10] "=&v"(t[1][0]), [t11] "=&v"(t[1][1]), [t12] "=&v"(t[1][2]), [t13] "=&v"(t[1][3])
+#define MOE_TR_INS(KP)                                                          \
+  [B0] "v"(b0), [B1] "v"(b1), [ob0] "i"((2 * KP) * 32 * kRowBytes),             \
+  [ob1] "i"((2 * KP + 1) * 32 * kRowBytes), [ow0] "i"((2 * KP) * 32 * kRowBytes + kWTile), \
+  [ow1] "i"((2 * KP + 1) * 32 * kRowBytes + kWTile), [oa0] "i"((2 * KP) * XS), [oa1] "i"((2 * KP + 1) * XS)
 
-template <int MTX, int NA>
+template <int NA, int KP, int XS>
+struct PairFrags;
+
+template <int KP, int XS>
+struct PairFrags<1, KP, XS> {
+  __device__ __forceinline__ static void read(uint32_t b0, uint32_t b1, const uint32_t (&xa)[4],
+                                              long (&t)[2][4], bf16x8_t (&a)[2][4]) {
+    asm volatile(MOE_TR_PAIR(0) MOE_TR_PAIR(1)
+                 "ds_read_b128 %[a00], %[X0] offset:%[oa0]\n\t"
+                 "ds_read_b128 %[a10], %[X0] offset:%[oa1]\n\t"
+                 "s_waitcnt lgkmcnt(0)"
+                 : MOE_TR_OUTS, [a00] "=&v"(a[0][0]), [a10] "=&v"(a[1][0])
+                 : MOE_TR_INS(KP), [X0] "v"(xa[0]));
+  }
+};
+template <int KP, int XS>
+struct PairFrags<2, KP, XS> {
+  __device__ __forceinline__ static void read(uint32_t b0, uint32_t b1, const uint32_t (&xa)[4],
+                                              long (&t)[2][4], bf16x8_t (&a)[2][4]) {
+    asm volatile(MOE_TR_PAIR(0) MOE_TR_PAIR(1)
+                 "ds_read_b128 %[a00], %[X0] offset:%[oa0]\n\t"
+                 "ds_read_b128 %[a01], %[X1] offset:%[oa0]\n\t"
+                 "ds_read_b128 %[a10], %[X0] offset:%[oa1]\n\t"
+                 "ds_read_b128 %[a11], %[X1] offset:%[oa1]\n\t"
+                 "s_waitcnt lgkmcnt(0)"
+                 : MOE_TR_OUTS, [a00] "=&v"(a[0][0]), [a01] "=&v"(a[0][1]), [a10] "=&v"(a[1][0]),
+                   [a11] "=&v"(a[1][1])
+                 : MOE_TR_INS(KP), [X0] "v"(xa[0]), [X1] "v"(xa[1]));
+  }
+};
+template <int KP, int XS>
+struct PairFrags<3, KP, XS> {
+  __device__ __forceinline__ static void read(uint32_t b0, uint32_t b1, const uint32_t (&xa)[4],
+                                              long (&t)[2][4], bf16x8_t (&a)[2][4]) {
+    asm volatile(MOE_TR_PAIR(0) MOE_TR_PAIR(1)
+                 "ds_read_b128 %[a00], %[X0] offset:%[oa0]\n\t"
+                 "ds_read_b128 %[a01], %[X1] offset:%[oa0]\n\t"
+                 "ds_read_b128 %[a02], %[X2] offset:%[oa0]\n\t"
+                 "ds_read_b128 %[a10], %[X0] offset:%[oa1]\n\t"
+                 "ds_read_b128 %[a11], %[X1] offset:%[oa1]\n\t"
+                 "ds_read_b128 %[a12], %[X2] offset:%[oa1]\n\t"
+                 "s_waitcnt lgkmcnt(0)"
+                 : MOE_TR_OUTS, [a00] "=&v"(a[0][0]), [a01] "=&v"(a[0][1]), [a02] "=&v"(a[0][2]),
+                   [a10] "=&v"(a[1][0]), [a11] "=&v"(a[1][1]), [a12] "=&v"(a[1][2])
+                 : MOE_TR_INS(KP), [X0] "v"(xa[0]), [X1] "v"(xa[1]), [X2] "v"(xa[2]));
+  }
+};
+template <int KP, int XS>
+struct PairFrags<4, KP, XS> {
+  __device__ __forceinline__ static void read(uint32_t b0, uint32_t b1, const uint32_t (&xa)[4],
+                                              long (&t)[2][4], bf16x8_t (&a)[2][4]) {
+    asm volatile(MOE_TR_PAIR(0) MOE_TR_PAIR(1)
+                 "ds_read_b128 %[a00], %[X0] offset:%[oa0]\n\t"
+                 "ds_read_b128 %[a01], %[X1] offset:%[oa0]\n\t"
+                 "ds_read_b128 %[a02], %[X2] offset:%[oa0]\n\t"
+                 "ds_read_b128 %[a03], %[X3] offset:%[oa0]\n\t"
+                 "ds_read_b128 %[a10], %[X0] offset:%[oa1]\n\t"
+                 "ds_read_b128 %[a11], %[X1] offset:%[oa1]\n\t"
+                 "ds_read_b128 %[a12], %[X2] offset:%[oa1]\n\t"
+                 "ds_read_b128 %[a13], %[X3] offset:%[oa1]\n\t"
+                 "s_waitcnt lgkmcnt(0)"
+                 : MOE_TR_OUTS, [a00] "=&v"(a[0][0]), [a01] "=&v"(a[0][1]), [a02] "=&v"(a[0][2]),
+                   [a03] "=&v"(a[0][3]), [a10] "=&v"(a[1][0]), [a11] "=&v"(a[1][1]),
+                   [a12] "=&v"(a[1][2]), [a13] "=&v"(a[1][3])
+                 : MOE_TR_INS(KP), [X0] "v"(xa[0]), [X1] "v"(xa[1]), [X2] "v"(xa[2]), [X3] "v"(xa[3]));
+  }
+};
+#undef MOE_TR_PAIR
+#undef MOE_TR_OUTS
+#undef MOE_TR_INS
+
+// MFMA work of one stage in two pairs of k-steps; hook(kp) runs before pair
+// kp (the loop issues half of a later stage's copies there, so that the
+// copies enter the memory pipeline while this stage computes).
+template <int MTX, int NA, class Hook>
 __device__ __forceinline__ void mfma_stage(uint32_t slot, uint32_t xslot, const uint32_t (&trc)[2],
-                                           uint32_t xrd, Acc &acc) {
+                                           uint32_t xrd, Acc &acc, const Hook &hook) {
+  constexpr int XS = Shape<2, MTX>::kXSub;
+  static_assert(kKSteps == 4, "two pairs of k-steps per stage");
+  const uint32_t b0 = slot + trc[0], b1 = slot + trc[1];
+  uint32_t xa[4];
 #pragma unroll
-  for (int ks = 0; ks < kKSteps; ++ks) {
-    bf16x8_t b[2];
-    b_frags(slot, trc, ks, b);
-    uint32_t aa[4];
+  for (int mt = 0; mt < 4; ++mt) xa[mt] = xslot + uint32_t(mt * 1024) + xrd;
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) aa[mt] = xslot + uint32_t(ks * Shape<2, MTX>::kXSub + mt * 1024) + xrd;
-    bf16x8_t a[4];
-    lds_b128<NA>(aa, a);
+  for (int kp = 0; kp < 2; ++kp) {
+    hook(kp);
+    long t[2][4];
+    bf16x8_t a[2][4];
+    if (kp == 0) PairFrags<NA, 0, XS>::read(b0, b1, xa, t, a);
+    else PairFrags<NA, 1, XS>::read(b0, b1, xa, t, a);
 #pragma unroll
-    for (int mt = 0; mt < NA; ++mt)
+    for (int q = 0; q < 2; ++q) {
+      bf16x8_t b[2];
+      __builtin_memcpy(&b[0], &t[q][0], 8);
+      __builtin_memcpy(reinterpret_cast<char *>(&b[0]) + 8, &t[q][1], 8);
+      __builtin_memcpy(&b[1], &t[q][2], 8);
+      __builtin_memcpy(reinterpret_cast<char *>(&b[1]) + 8, &t[q][3], 8);
 #pragma unroll
-      for (int mat = 0; mat < 2; ++mat)
-        acc.mf[mat][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[mt], b[mat], acc.mf[mat][mt], 0, 0, 0);
+      for (int mt = 0; mt < NA; ++mt)
+#pragma unroll
+        for (int mat = 0; mat < 2; ++mat)
+          acc.mf[mat][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[q][mt], b[mat], acc.mf[mat][mt], 0, 0, 0);
+    }
   }
 }
 
-template <int MTX>
+template <int MTX, class Hook>
 __device__ __forceinline__ void compute_stage(uint32_t slot, const uint32_t (&trc)[2], uint32_t xrd,
-                                              int T, Acc &acc) {
+                                              int T, Acc &acc, const Hook &hook) {
   const uint32_t xslot = slot + 2 * kWTile;
   const int na = (T + 15) >> 4;
-  if (MTX == 1 || na == 1) mfma_stage<MTX, 1>(slot, xslot, trc, xrd, acc);
-  else if (MTX == 2 || na == 2) mfma_stage<MTX, (MTX >= 2 ? 2 : 1)>(slot, xslot, trc, xrd, acc);
-  else if (na == 3) mfma_stage<MTX, (MTX >= 3 ? 3 : 1)>(slot, xslot, trc, xrd, acc);
-  else mfma_stage<MTX, (MTX >= 4 ? 4 : 1)>(slot, xslot, trc, xrd, acc);
+  if (MTX == 1 || na == 1) mfma_stage<MTX, 1>(slot, xslot, trc, xrd, acc, hook);
+  else if (MTX == 2 || na == 2) mfma_stage<MTX, (MTX >= 2 ? 2 : 1)>(slot, xslot, trc, xrd, acc, hook);
+  else if (na == 3) mfma_stage<MTX, (MTX >= 3 ? 3 : 1)>(slot, xslot, trc, xrd, acc, hook);
+  else mfma_stage<MTX, (MTX >= 4 ? 4 : 1)>(slot, xslot, trc, xrd, acc, hook);
 }
 
 // Stores the accumulators of the pass that just ended: the gate and up partial
@@ -871,13 +922,18 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_kernel(Params p,
       case 2: wait_barrier<(kD - 1 >= 2 ? 2 : 0) * S::kCopies>(); break;
       default: wait_barrier<(kD - 1 >= 3 ? 3 : 0) * S::kCopies>(); break;
     }
-    // Every wave is past stage s-1, so its slot takes stage s+kD.
-    if (prod.valid && (prod.up || h_ready)) {
-      st.issue(prod, stages + ((s + kD) % kS) * S::kSlot);
+    // Every wave is past stage s-1, so its slot takes stage s+kD, whose
+    // copies are issued in two halves during the compute of stage s.
+    const bool fill = prod.valid && (prod.up || h_ready);
+    unsigned char *fslot = stages + ((s + kD) % kS) * S::kSlot;
+    compute_stage<MTX>(base + uint32_t((s % kS) * S::kSlot), st.trc, st.xrd, st.tp(cons), acc,
+                       [&](int half) {
+                         if (fill) st.issue_half(prod, fslot, half);
+                       });
+    if (fill) {
       ++issued;
       st.advance(prod);
     }
-    compute_stage<MTX>(base + uint32_t((s % kS) * S::kSlot), st.trc, st.xrd, st.tp(cons), acc);
     if (cons.kst == cons.nst - 1) {
       epilogue<MTX>(cons, p, st.meta, st.wave, st.lane, acc);
       clear(acc);
