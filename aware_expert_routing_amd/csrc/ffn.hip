@@ -90,14 +90,17 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
 
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
 
-// XOR applied to the 16-byte chunk index of weight row r of a stage. The
-// transposing reads of one instruction touch rows kk + 8g + 4h + {0..3}
-// (g = 0..3); this map spreads their chunk pairs over the banks, and it does
-// not depend on kk (a multiple of 32), so a lane's read offsets are constants.
-__device__ __forceinline__ int swz_w(int r) { return (((r >> 1) ^ (r >> 3)) & 3) << 1; }
-// Chunk XOR of A-tile row m (rows of 64 bytes = 4 chunks): the 16 rows a
-// fragment reads at one logical chunk hit 16 distinct 4-bank groups.
-__device__ __forceinline__ int swz_x(int m) { return (m >> 2) & 3; }
+// XOR applied to the 16-byte chunk index of weight row r of a stage (an even
+// value, so chunk pairs 2c, 2c+1 stay together). The 16 lanes of group g of a
+// transposing read take rows kk + 8g + 4h + {0..3}, 32 bytes (one chunk pair)
+// each; the XOR differs between those four rows, so the group covers all 32
+// banks once. It does not depend on kk (a multiple of 32), so a lane's read
+// offsets are constants.
+__device__ __forceinline__ int swz_w(int r) { return ((r ^ (r >> 2)) & 3) << 1; }
+// Chunk XOR of A-tile row m (rows of 64 bytes = 4 chunks): the 8 lanes
+// (rows j..j+7, one logical chunk) that a 16-byte read serves together hit 8
+// distinct 4-bank groups.
+__device__ __forceinline__ int swz_x(int m) { return (m >> 1) & 3; }
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, int(bytes), kRsrcWord3);
