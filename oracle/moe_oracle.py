@@ -52,10 +52,32 @@ Readings where the pages are silent (each is stated where it is used):
       its tokens takes the first min(k, m_r) experts of its own order inside
       S_r. Both levels maximise the total gating score under their budget,
       the modular objective of [XShare].
+  R9  lynx(m), a confidence-gated remap ([Lynx] section 2.1 "Token
+      Confidence" and "Expert Rank Hierarchy", section 2.2 "Confidence
+      Analyzer", "Adaptive Expert Scorer", "Expert Remapper"; the page gives
+      no formulas, so every constant below is this build's reading):
+      * confidence of token t's rank-j expert (j < k) is the logit gap
+        delta = L[t, rank 0] - L[t, rank j] (float32 subtraction);
+      * AffinityBinning: k bins of width w = ln(E / k) (the inverse sparsity
+        ratio N/k on a logit scale), rounded to float32; the bin is the
+        number of i in 1..k-1 with delta >= float32(i) * w (float32
+        product), i.e. min(k - 1, floor(delta / w));
+      * the expert scorer adds 2^(k - 1 - bin) for every (token, rank < k)
+        pair naming the expert (an integer: confident pairs weigh
+        exponentially more);
+      * the critical set C holds every token's rank-0 expert (rank 0 is
+        kept), then the other experts named by some token's top-k, by score
+        descending (ties to the lower index), until |C| = max(m, |R0|) or
+        no such expert is left;
+      * the remapper gives token t the first k experts of its own order
+        inside C. With k <= m every token keeps exactly k experts, as the
+        page requires.
 
 Parity status of each function is listed in its docstring ("pinned by ...").
 """
 from __future__ import annotations
+
+import math
 
 import numpy as np
 
@@ -64,6 +86,7 @@ POLICY_OEA = "oea"
 POLICY_BUDGET = "budget"
 POLICY_GREEDY = "greedy"
 POLICY_HIER = "hier"
+POLICY_LYNX = "lynx"
 
 
 # ---------------------------------------------------------------- precision
@@ -309,6 +332,68 @@ def select_hier(L32: np.ndarray, k: int, m: int, m_r: int, g: int, mass=None) ->
     return _ids_matrix([_first_in(token_order(l), S[t // g], k) for t, l in enumerate(L32)], k)
 
 
+def lynx_bin_width(E: int, k: int) -> np.float32:
+    """AffinityBinning width (reading R9): ln(E / k) rounded to float32."""
+    return np.float32(math.log(E / k))
+
+
+def lynx_scores(L32: np.ndarray, k: int) -> np.ndarray:
+    """Adaptive expert scores (reading R9): for every token and each of its
+    k best experts, 2^(k - 1 - bin) with bin the token's confidence bin for
+    that expert. int64 [E].
+
+    Pinned by: a hand-worked example; invariance under token permutation.
+    """
+    B, E = L32.shape
+    w = lynx_bin_width(E, k)
+    thr = [np.float32(np.float32(i) * w) for i in range(1, k)]
+    score = np.zeros(E, dtype=np.int64)
+    for l in np.asarray(L32, dtype=np.float32):
+        o = token_order(l)
+        top = np.float32(l[o[0]])
+        for j in range(k):
+            delta = np.float32(top - np.float32(l[o[j]]))
+            b = sum(1 for t in thr if delta >= t)
+            score[o[j]] += 1 << (k - 1 - b)
+    return score
+
+
+def lynx_critical_set(L32: np.ndarray, k: int, m: int) -> np.ndarray:
+    """The critical set C of lynx(m) (reading R9). Boolean mask [E].
+
+    Pinned by: C holds every rank-0 expert; |C| = min(max(m, |R0|), |U|)
+    with U the union of the tokens' top-k; C(m) is inside C(m + 1);
+    m <= |R0| gives R0.
+    """
+    B, E = L32.shape
+    score = lynx_scores(L32, k)
+    C = np.zeros(E, dtype=bool)
+    named = np.zeros(E, dtype=bool)
+    for l in np.asarray(L32, dtype=np.float32):
+        o = token_order(l)
+        C[o[0]] = True
+        named[o[:k]] = True
+    n0 = int(C.sum())
+    rest = [e for e in range(E) if named[e] and not C[e]]
+    rest.sort(key=lambda e: (-score[e], e))
+    C[rest[:max(0, m - n0)]] = True
+    return C
+
+
+def select_lynx(L32: np.ndarray, k: int, m: int) -> np.ndarray:
+    """lynx(m) (reading R9): each token takes the first k experts of its own
+    order inside the critical set. ids [B, k].
+
+    Pinned by: exactly k distinct experts per token with rank 0 in slot 0;
+    m >= |U| equals topk; k <= m <= |R0| equals oea(k0 = 1).
+    """
+    B, E = L32.shape
+    if not 1 <= k <= m <= E:
+        raise ValueError("lynx needs 1 <= k <= m <= E")
+    C = lynx_critical_set(L32, k, m)
+    return _ids_matrix([_first_in(token_order(l), C, k) for l in L32], k)
+
+
 def select(L32: np.ndarray, policy: str, k: int, k0: int = 0, m: int = 0, g: int = 0):
     """Dispatch on policy name. Returns (ids [B,k] int32, mass or None).
     hier takes m (batch budget), k0 (the request budget m_r) and g (tokens per
@@ -330,6 +415,8 @@ def select(L32: np.ndarray, policy: str, k: int, k0: int = 0, m: int = 0, g: int
     if policy == POLICY_HIER:
         M = budget_mass(L32)
         return select_hier(L32, k, m, k0, g, M), M
+    if policy == POLICY_LYNX:
+        return select_lynx(L32, k, m), None
     raise ValueError(policy)
 
 

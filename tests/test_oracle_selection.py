@@ -422,3 +422,77 @@ def test_hier_argument_checks():
         orc.request_sets(L, 4, 5, 2)   # m_r > m
     with pytest.raises(ValueError):
         orc.request_sets(L, 4, 2, 0)   # g < 1
+
+
+# ------------------------------------------------------------------ lynx(m)
+
+def test_lynx_hand_worked_scores():
+    """The expert scores of the hand-worked lynx examples (confidence bins
+    and exponential weights worked out by hand in the fixture)."""
+    with open(GOLDEN) as f:
+        ex = [e for e in json.load(f)["examples"] if "lynx_scores" in e]
+    assert len(ex) == 2
+    for e in ex:
+        L = _logits_from_json(e["logits"])
+        assert orc.lynx_scores(L, e["k"]).tolist() == e["lynx_scores"]
+
+
+def _rank0_and_union(L, k):
+    R0, U = set(), set()
+    for l in L:
+        order = sorted(range(L.shape[1]), key=lambda e: (-float(l[e]), e))
+        R0.add(order[0])
+        U.update(order[:k])
+    return R0, U
+
+
+@pytest.mark.parametrize("seed", range(4))
+@pytest.mark.parametrize("shape", [(16, 128, 8), (8, 64, 6), (32, 16, 4), (5, 12, 3)])
+def test_lynx_invariants(seed, shape):
+    """Exactly k distinct experts per token with its rank-0 expert in slot 0;
+    C holds R0 and has min(max(m, |R0|), |U|) experts, all named by some
+    token's top-k; C grows with m; every token takes the first k of its own
+    order inside C."""
+    B, E, k = shape
+    L = make_logits(B, E, seed=seed)
+    R0, U = _rank0_and_union(L, k)
+    prev = set()
+    for m in range(k, E + 1, max(1, (E - k) // 7)):
+        C = set(np.flatnonzero(orc.lynx_critical_set(L, k, m)).tolist())
+        assert R0 <= C <= U
+        assert len(C) == min(max(m, len(R0)), len(U))
+        assert prev <= C
+        prev = C
+        ids = orc.select_lynx(L, k, m)
+        for t in range(B):
+            order = sorted(range(E), key=lambda e: (-float(L[t, e]), e))
+            assert ids[t, 0] == order[0]
+            assert len(set(ids[t].tolist())) == k and (ids[t] >= 0).all()
+            assert ids[t].tolist() == [e for e in order if e in C][:k]
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_lynx_reductions(seed):
+    """m >= |U| gives topk; k <= m <= |R0| gives oea(k0 = 1) (C = R0)."""
+    for B, E, k in ((16, 128, 8), (64, 32, 4), (40, 16, 2)):
+        L = make_logits(B, E, seed=100 + seed)
+        R0, U = _rank0_and_union(L, k)
+        assert np.array_equal(orc.select_lynx(L, k, E), orc.select_topk(L, k))
+        assert np.array_equal(orc.select_lynx(L, k, len(U)), orc.select_topk(L, k))
+        for m in range(k, len(R0) + 1):
+            assert np.array_equal(orc.select_lynx(L, k, m), orc.select_oea(L, k, 1))
+
+
+def test_lynx_scores_ignore_token_order():
+    L = make_logits(24, 64, seed=7)
+    perm = np.random.default_rng(3).permutation(24)
+    assert np.array_equal(orc.lynx_scores(L, 6), orc.lynx_scores(L[perm], 6))
+    assert np.array_equal(orc.lynx_critical_set(L, 6, 20), orc.lynx_critical_set(L[perm], 6, 20))
+
+
+def test_lynx_argument_checks():
+    L = make_logits(4, 16, seed=1)
+    with pytest.raises(ValueError):
+        orc.select_lynx(L, 4, 3)    # m < k: exactly k per token impossible
+    with pytest.raises(ValueError):
+        orc.select_lynx(L, 4, 17)   # m > E
