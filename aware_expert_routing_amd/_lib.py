@@ -28,6 +28,7 @@ MOE_POLICY_OEA = 1
 MOE_POLICY_BUDGET = 2
 MOE_POLICY_GREEDY = 3
 MOE_POLICY_HIER = 4
+MOE_POLICY_LYNX = 5
 
 EXPORTS = ("moe_workspace_bytes", "moe_route", "moe_select", "moe_expert_ffn",
            "moe_layer_decode", "moe_status_string", "moe_read_stream")
@@ -97,9 +98,9 @@ def _check(status: int):
 
 def make_policy(kind: str, k: int, k0: int = 0, m: int = 0, g: int = 0) -> Policy:
     """kind: topk | oea (k0) | budget (m) | greedy (m) | hier (m, k0 = request
-    budget m_r, g = tokens per request)."""
+    budget m_r, g = tokens per request) | lynx (m, the critical-set size)."""
     kinds = {"topk": MOE_POLICY_TOPK, "oea": MOE_POLICY_OEA, "budget": MOE_POLICY_BUDGET,
-             "greedy": MOE_POLICY_GREEDY, "hier": MOE_POLICY_HIER}
+             "greedy": MOE_POLICY_GREEDY, "hier": MOE_POLICY_HIER, "lynx": MOE_POLICY_LYNX}
     if kind not in kinds:
         raise ValueError(f"unknown policy {kind!r}")
     return Policy(kinds[kind], int(k), int(k0), int(m), int(g))

@@ -35,6 +35,8 @@ moe_status_t check_policy(const moe_policy_t &p, int E) {
     case MOE_POLICY_HIER:
       return (p.m >= 1 && p.m <= E && p.k0 >= 1 && p.k0 <= p.m && p.g >= 1) ? MOE_OK
                                                                              : MOE_ERR_INVALID_ARG;
+    case MOE_POLICY_LYNX:
+      return (p.m >= p.k && p.m <= E) ? MOE_OK : MOE_ERR_INVALID_ARG;
     default:
       return MOE_ERR_INVALID_ARG;
   }

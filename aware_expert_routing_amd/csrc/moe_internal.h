@@ -4,6 +4,7 @@
 
 #include <hip/hip_runtime.h>
 #include <stddef.h>
+#include <cmath>
 #include <stdint.h>
 
 #include "../../include/moe_decode.h"
@@ -30,6 +31,10 @@ constexpr int kStageRows = 128;     // weight rows staged in LDS per pipeline st
 inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
 inline size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
+
+// Width of the LYNX policy's confidence bins: ln(E / k), rounded to float32
+// once on the host so that every kernel compares against the same value.
+inline float lynx_bin_width(int E, int k) { return float(std::log(double(E) / double(k))); }
 
 // The first kCounterBytes of every workspace hold counters at fixed offsets
 // (the same for every size of call, so that calls of different sizes may

@@ -33,7 +33,7 @@ template <bool VEC, int NV, int TPW>
 __global__ __launch_bounds__(kThreads) void route_select_kernel(
     const uint16_t *__restrict__ x, const uint16_t *__restrict__ w, const float *__restrict__ bias,
     int B, int d, int E, float *__restrict__ logits, float *__restrict__ part,
-    uint32_t *__restrict__ cnt, int kind, int k, int k0, int m, int g,
+    uint32_t *__restrict__ cnt, int kind, int k, int k0, int m, int g, float bin_w,
     int32_t *__restrict__ topk_ids, float *__restrict__ topk_w, int32_t *__restrict__ n_active,
     int32_t *__restrict__ active_experts, int32_t *__restrict__ expert_offsets,
     int32_t *__restrict__ pair_token, int32_t *__restrict__ pair_slot,
@@ -58,7 +58,7 @@ __global__ __launch_bounds__(kThreads) void route_select_kernel(
   __syncthreads();
   if (!s_last) return;
   select_block<NV, TPW>(SliceLogits{part, bias, logits, E, int(gridDim.x), slices}, B, E, kind, k, k0,
-                        m, g, topk_ids, topk_w, n_active, active_experts, expert_offsets, pair_token,
+                        m, g, bin_w, topk_ids, topk_w, n_active, active_experts, expert_offsets, pair_token,
                         pair_slot, batch_mass);
 }
 
@@ -69,7 +69,8 @@ void launch_rs(dim3 grid, const uint16_t *x, const uint16_t *w, const float *bia
   float *mass = (p.kind == MOE_POLICY_BUDGET || p.kind == MOE_POLICY_HIER) ? r.batch_mass : nullptr;
   dispatch_select_shape(B, E, [&](auto nv, auto tpw) {
     route_select_kernel<VEC, decltype(nv)::value, decltype(tpw)::value><<<grid, kThreads, 0, s>>>(
-        x, w, bias, B, d, E, logits, part, cnt, p.kind, p.k, p.k0, p.m, p.g, r.topk_ids, r.topk_w,
+        x, w, bias, B, d, E, logits, part, cnt, p.kind, p.k, p.k0, p.m, p.g, lynx_bin_width(E, p.k),
+        r.topk_ids, r.topk_w,
         r.n_active, r.active_experts, r.expert_offsets, r.pair_token, r.pair_slot, mass);
   });
 }

@@ -25,6 +25,16 @@
 //             r*g+g-1) keeps the m_r experts of that set with the largest
 //             mass summed over its own tokens, in token order (ties to the
 //             lower index); its tokens rank inside that request set.
+//   LYNX(m)   "Lynx", Technical Summary 2.1 and 2.2 (the constants are
+//             this build's reading): the gap between a token's rank-0 logit
+//             and each of its top-k logits (float32) falls into one of k
+//             bins of width bin_w = ln(E/k) (bin = number of i in 1..k-1 with
+//             gap >= i * bin_w, float32 products); an expert scores
+//             2^(k-1-bin) per (token, rank < k) naming it (integer sums, so
+//             the order of the atomics does not matter); the critical set
+//             holds every rank-0 expert plus the best-scored other named
+//             experts (ties to the lower index) up to max(m, |rank-0 set|);
+//             tokens take their first k experts inside it.
 //   weights   softmax over each token's selected logits.
 //   compact   "Lynx", Technical Summary 2.2: the batch activates one
 //             consolidated expert set; this kernel lists it (ascending) and
@@ -170,6 +180,32 @@ __device__ __forceinline__ int wave_rank(uint32_t (&key)[NV], int rounds, int ba
 
 __device__ __forceinline__ bool bit_of(const uint32_t *mask, int e) { return (mask[e >> 5] >> (e & 31)) & 1u; }
 
+// Descending rank of every key among key[0..E) (ties to the lower index),
+// added into rank[] (zero before; read after a barrier): rank[e] counts the
+// e2 with key[e2] > key[e], or key[e2] == key[e] and e2 < e. The E x E
+// comparisons are spread over the whole workgroup: thread (part, e) compares
+// key[e] with a quarter of the keys, 16 bytes per LDS read, and adds its
+// count with one LDS atomic (integer, so the sum does not depend on order).
+// key must be 16-byte aligned with room for kMaxE entries.
+__device__ __forceinline__ void rank_keys_desc(const uint32_t *key, int E, int *rank) {
+  constexpr int kParts = kThreads / kMaxE;
+  static_assert(kParts * kMaxE == kThreads && kMaxE % (4 * kParts) == 0, "rank split");
+  const int e = threadIdx.x % kMaxE, part = threadIdx.x / kMaxE;
+  if (e >= E) return;
+  const uint32_t ke = key[e];
+  const int span = (((E + kParts - 1) / kParts) + 3) & ~3;
+  const int lo = part * span, hi = min(E, lo + span);
+  int r = 0;
+  for (int e0 = lo; e0 < hi; e0 += 4) {
+    const uint4 o = *reinterpret_cast<const uint4 *>(key + e0);
+    r += e0 < hi && ((o.x > ke) || (o.x == ke && e0 < e));
+    r += e0 + 1 < hi && ((o.y > ke) || (o.y == ke && e0 + 1 < e));
+    r += e0 + 2 < hi && ((o.z > ke) || (o.z == ke && e0 + 2 < e));
+    r += e0 + 3 < hi && ((o.w > ke) || (o.w == ke && e0 + 3 < e));
+  }
+  if (r) atomicAdd(&rank[e], r);
+}
+
 // Source of the float32 logits: logit(t, e) with 0 <= t < B, 0 <= e < E,
 // and emit(t, e, v), called once for every (t, e) with the value read.
 // Logits stored in memory: device-scope loads (another workgroup of the same
@@ -188,7 +224,7 @@ struct StoredLogits {
 // phases are unrolled over the slots, so a small TPW keeps the code small.
 template <int NV, int TPW, class Src>
 __device__ __forceinline__ void select_block(
-    const Src &src, int B, int E, int kind, int k, int k0, int m, int g,
+    const Src &src, int B, int E, int kind, int k, int k0, int m, int g, float bin_w,
     int32_t *__restrict__ topk_ids, float *__restrict__ topk_w, int32_t *__restrict__ n_active,
     int32_t *__restrict__ active_experts, int32_t *__restrict__ expert_offsets,
     int32_t *__restrict__ pair_token, int32_t *__restrict__ pair_slot,
@@ -199,13 +235,16 @@ __device__ __forceinline__ void select_block(
   __shared__ int16_t sel_id[kMaxB][kMaxK];
   __shared__ float sel_w[kMaxB][kMaxK];
   __shared__ float psum[kWaves][kMaxE];
-  __shared__ float mass[kMaxE];
+  __shared__ __attribute__((aligned(16))) float mass[kMaxE];
+  __shared__ int krank[kMaxE];  // BUDGET, HIER, LYNX: rank of each expert's key
   __shared__ int acnt[kMaxE];
   __shared__ int apos[kMaxE];
   __shared__ int aoff[kMaxE];
   __shared__ int s_n, s_total;
   __shared__ float tok_mx[kMaxB], tok_sm[kMaxB], tok_thr[kMaxB];  // GREEDY per-token state
   __shared__ int tok_cnt[kMaxB];
+  __shared__ __attribute__((aligned(16))) uint32_t lscore[kMaxE];  // LYNX: expert scores
+  __shared__ uint32_t lrank0[kWords];  // LYNX: rank-0 experts of the batch
   __shared__ uint32_t w_best[kWaves];
   __shared__ int w_e[kWaves];
   __shared__ int s_pick;
@@ -224,6 +263,11 @@ __device__ __forceinline__ void select_block(
     allowed[i] = full;
   }
   for (int i = tid; i < kMaxE * kTokWords; i += kThreads) etok[i / kTokWords][i % kTokWords] = 0;
+  if (kind == MOE_POLICY_LYNX) {
+    for (int i = tid; i < kMaxE; i += kThreads) lscore[i] = 0;
+    for (int i = tid; i < kWords; i += kThreads) lrank0[i] = 0;
+  }
+  for (int i = tid; i < kMaxE; i += kThreads) krank[i] = 0;
   if (kind == MOE_POLICY_HIER)
     for (int i = tid; i < ((B + g - 1) / g) * kWords; i += kThreads) req_allowed[i / kWords][i % kWords] = 0;
 
@@ -309,14 +353,11 @@ __device__ __forceinline__ void select_block(
     }
     if (tid < E) mass[tid] = macc;
     __syncthreads();
-    if (tid < E) {
-      int rank = 0;
-      for (int e2 = 0; e2 < E; ++e2) {
-        const float o = mass[e2];
-        rank += (o > macc) || (o == macc && e2 < tid);
-      }
-      if (rank < m) atomicOr(&allowed[tid >> 5], 1u << (tid & 31));
-    }
+    // Masses are sums of non-negative terms (never -0.0), so their bit
+    // patterns order like the values.
+    rank_keys_desc(reinterpret_cast<const uint32_t *>(mass), E, krank);
+    __syncthreads();
+    if (tid < E && krank[tid] < m) atomicOr(&allowed[tid >> 5], 1u << (tid & 31));
     if (kind == MOE_POLICY_HIER) {
       // Request level: wave w takes requests w, w+16, ...; a request's mass
       // is summed over its tokens in order (each token's softmax recomputed
@@ -368,6 +409,44 @@ __device__ __forceinline__ void select_block(
         const int n = wave_rank<NV>(key, k0, 0, lane, pe, pk, ptop);
         if (lane < n) atomicOr(&req_allowed[r][pe >> 5], 1u << (pe & 31));
       }
+    }
+  } else if (kind == MOE_POLICY_LYNX) {
+    // Confidence bins of each token's top-k and the experts' scores.
+#pragma unroll
+    for (int ti = 0; ti < TPW; ++ti) {
+      const int t = wave + kWaves * ti;
+      if (t < B) {
+        uint32_t key[NV];
+#pragma unroll
+        for (int v = 0; v < NV; ++v) key[v] = (lane + 64 * v < E) ? ord_bits(L[ti][v]) : 0u;
+        int e = 0;
+        uint32_t kv = 0, top = 0;
+        const int n = wave_rank<NV>(key, k, 0, lane, e, kv, top);
+        if (lane < n) {
+          const float gap = from_ord_bits(top) - from_ord_bits(kv);
+          int bin = 0;
+          for (int i = 1; i < k; ++i) bin += gap >= float(i) * bin_w;
+          atomicAdd(&lscore[e], 1u << (k - 1 - bin));
+          if (lane == 0) atomicOr(&lrank0[e >> 5], 1u << (e & 31));
+        }
+      }
+    }
+    __syncthreads();
+    // Critical set: the rank-0 experts, then the other named experts (score
+    // > 0) by score descending, ties to the lower index. Rank-0 experts drop
+    // out of the ranking (score set to 0, as for experts nobody named).
+    const bool rank0 = tid < E && bit_of(lrank0, tid);
+    if (rank0) lscore[tid] = 0;
+    __syncthreads();
+    rank_keys_desc(lscore, E, krank);
+    __syncthreads();
+    if (tid < E) {
+      int n0 = 0;
+      for (int w = 0; w < kWords; ++w) n0 += __popc(lrank0[w]);
+      // A named expert's score is at least 1, so zero keys (rank-0 and
+      // unnamed experts) never rank above one.
+      const bool keep = rank0 || (lscore[tid] > 0 && krank[tid] < m - n0);
+      if (keep) atomicOr(&allowed[tid >> 5], 1u << (tid & 31));
     }
   } else if (kind == MOE_POLICY_GREEDY) {
     // Per-token softmax normalisers (probabilities are recomputed from the

@@ -40,7 +40,7 @@ def _parse():
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--config", default="qwen3_30b_bf16")
     ap.add_argument("--batch", type=int, default=16)
-    ap.add_argument("--policy", default="oea", choices=["topk", "oea", "budget", "greedy", "hier"])
+    ap.add_argument("--policy", default="oea", choices=["topk", "oea", "budget", "greedy", "hier", "lynx"])
     ap.add_argument("--k0", type=int, default=4)
     ap.add_argument("--m", type=int, default=32)
     ap.add_argument("--g", type=int, default=4, help="hier: tokens per request (--k0 is the request budget)")
@@ -200,7 +200,7 @@ def _cpu_baseline(cfg, inp, B, policy, k0, m, active_bytes, seconds, g=0):
 
 def _policy_name(policy, k0, m, g):
     return policy + {"oea": f"(k0={k0})", "budget": f"(m={m})", "greedy": f"(m={m})",
-                     "hier": f"(m={m},m_r={k0},g={g})"}.get(policy, "")
+                     "hier": f"(m={m},m_r={k0},g={g})", "lynx": f"(m={m})"}.get(policy, "")
 
 
 def _run_case(cfg, B, policy, k0, m, inp, dev, args, with_cpu, g=0):
@@ -322,6 +322,8 @@ def main():
                        [("budget", 0, m, 0) for m in cfg.budget_m]
                 if cname == "specdec_bf16":  # requests of 4 drafts
                     pols += [("hier", m // 4, m, 4) for m in cfg.budget_m]
+                if cname in ("qwen3_30b_bf16", "lynx_bf16"):
+                    pols += [("lynx", 0, m, 0) for m in cfg.budget_m if m >= cfg.k]
                 for B in cfg.batches:
                     for pol, k0, m, g in pols:
                         rec = _run_case(cfg, B, pol, k0, m, inp, dev, args, with_cpu=False, g=g)

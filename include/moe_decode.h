@@ -35,6 +35,19 @@
  *                              its request's set ("XShare", summary and
  *                              abstract: hierarchical selection for
  *                              speculative decoding; this build's reading).
+ *                   LYNX(m)    confidence-gated remap ("Lynx", Technical
+ *                              Summary 2.1 and 2.2; constants are this
+ *                              build's reading): the gap between a token's
+ *                              rank-0 logit and each of its top-k logits is
+ *                              binned into k bins of width ln(E/k) (float32);
+ *                              an expert scores 2^(k-1-bin) per (token, rank
+ *                              < k) naming it; the critical set holds every
+ *                              token's rank-0 expert plus the best-scored
+ *                              other experts named by some top-k (ties to the
+ *                              lower index), max(m, |rank-0 set|) in all, as
+ *                              far as there are such experts; each token
+ *                              takes its first k experts inside it, so every
+ *                              token keeps exactly k.
  *   4. weights:   gate weights are the softmax over each token's selected
  *                 logits (renormalised); empty slots weigh 0.
  *   5. compaction: the ascending list of active experts and, per active
@@ -93,13 +106,15 @@ typedef enum {
   MOE_POLICY_OEA = 1,    /* 1 <= k0 <= k; tokens get min(k, |S|) experts         */
   MOE_POLICY_BUDGET = 2, /* 1 <= m <= E; tokens get min(k, m) experts            */
   MOE_POLICY_GREEDY = 3, /* 1 <= m <= E; tokens get min(k, m) experts            */
-  MOE_POLICY_HIER = 4    /* 1 <= k0 = m_r <= m <= E, g >= 1; tokens get
+  MOE_POLICY_HIER = 4,   /* 1 <= k0 = m_r <= m <= E, g >= 1; tokens get
                             min(k, m_r) experts                                  */
+  MOE_POLICY_LYNX = 5    /* k <= m <= E; tokens get exactly k experts            */
 } moe_policy_kind_t;
 
 /* Selection policy. k0 is read by OEA (its k0) and HIER (the request budget
- * m_r); m by BUDGET, GREEDY and HIER (the batch budget); g only by HIER
- * (tokens per request: token t belongs to request t / g). */
+ * m_r); m by BUDGET, GREEDY, HIER (the batch budget) and LYNX (the size of
+ * the critical set); g only by HIER (tokens per request: token t belongs to
+ * request t / g). */
 typedef struct {
   int32_t kind; /* moe_policy_kind_t */
   int32_t k;

@@ -55,7 +55,7 @@ class Guarded:
 
 def policy_args(policy: str, p):
     """Policy parameters as keyword arguments; p is k0 (oea), m (budget,
-    greedy) or the tuple (m, m_r, g) (hier: m_r travels as k0)."""
+    greedy, lynx) or the tuple (m, m_r, g) (hier: m_r travels as k0)."""
     if policy == "topk":
         return dict(policy="topk", k0=0, m=0, g=0)
     if policy == "oea":
@@ -64,6 +64,8 @@ def policy_args(policy: str, p):
         return dict(policy="budget", k0=0, m=p, g=0)
     if policy == "greedy":
         return dict(policy="greedy", k0=0, m=p, g=0)
+    if policy == "lynx":
+        return dict(policy="lynx", k0=0, m=p, g=0)
     if policy == "hier":
         m, m_r, g = p
         return dict(policy="hier", k0=m_r, m=m, g=g)

@@ -103,6 +103,9 @@ def _layer(lib, **kw):
     (dict(pol=L.Policy(L.MOE_POLICY_HIER, 8, 33, 32, 4)), L.MOE_ERR_INVALID_ARG),  # m_r > m
     (dict(pol=L.Policy(L.MOE_POLICY_HIER, 8, 8, 32, 0)), L.MOE_ERR_INVALID_ARG),  # g < 1
     (dict(pol=L.Policy(L.MOE_POLICY_HIER, 8, 8, 129, 4)), L.MOE_ERR_INVALID_ARG),  # m > E
+    (dict(pol=L.Policy(L.MOE_POLICY_LYNX, 8, 0, 7)), L.MOE_ERR_INVALID_ARG),      # m < k
+    (dict(pol=L.Policy(L.MOE_POLICY_LYNX, 8, 0, 129)), L.MOE_ERR_INVALID_ARG),    # m > E
+    (dict(pol=L.Policy(6, 8, 0, 32)), L.MOE_ERR_INVALID_ARG),                     # unknown kind
     (dict(pol=L.Policy(L.MOE_POLICY_HIER, 8, 8, 32, 4), r=_routing(mass=False)), L.MOE_ERR_INVALID_ARG),
     (dict(pol=L.Policy(7, 8, 0, 0)), L.MOE_ERR_INVALID_ARG),
     (dict(ws=None), L.MOE_ERR_WORKSPACE),

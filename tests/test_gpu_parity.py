@@ -129,7 +129,15 @@ def _hier_layer_cases():
                             ("tiny_f32", 4, (8, 4, 2)))]
 
 
-@pytest.mark.parametrize("cname,B,policy,p", _layer_cases() + _greedy_layer_cases() + _hier_layer_cases())
+def _lynx_layer_cases():
+    return [pytest.param(c, B, "lynx", m, id=f"{c}-B{B}-lynx{m}")
+            for c, B, m in (("tiny_f32", 4, 4), ("tiny_f32", 4, 10), ("lynx_bf16", 16, 24),
+                            ("qwen3_30b_bf16", 16, 16), ("qwen3_30b_bf16", 16, 24),
+                            ("qwen3_30b_bf16", 32, 32), ("specdec_bf16", 64, 32))]
+
+
+@pytest.mark.parametrize("cname,B,policy,p",
+                         _layer_cases() + _greedy_layer_cases() + _hier_layer_cases() + _lynx_layer_cases())
 def test_layer_matches_oracle(cname, B, policy, p):
     cfg = CONFIGS[cname]
     inp, dev = _layer_inputs(cname)
@@ -242,6 +250,7 @@ def _sel_policies(E, k, B):
     mb = max(1, E // 2)
     out += [("hier", p) for p in sorted({(mb, max(1, min(mb, k // 2)), 2), (mb, min(mb, k + 2), 4),
                                           (E, max(1, k - 1), 1), (mb, max(1, mb // 2), B)})]
+    out += [("lynx", m) for m in sorted({k, max(k, E // 4), max(k, E // 2), E})]
     return out
 
 
