@@ -47,6 +47,7 @@ constexpr int kRowBytes = kStripCols * 2;       // one strip row of bf16
 constexpr int kWTile = kBK * kRowBytes;         // bytes of one weight matrix per stage
 constexpr int kMaxTok = 64;                     // tokens per pass (4 MFMA row tiles)
 constexpr int kMaxPairs = kMaxB * kMaxK;
+constexpr int kSliceCost = 8;  // stages' worth of time the sliced gate/up path adds (measured)
 constexpr int kRsrcWord3 = 0x00020000;          // raw buffer, gfx9 data format
 constexpr int kLdsBytes = 160 * 1024;
 static_assert(kStripCols == 64 && kBK == 128, "tile constants");
@@ -880,9 +881,21 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_kernel(Params p,
   // strip of I) fill enough of the grid to keep HBM busy: each tile then
   // forms its h columns itself and the grid meets once. Otherwise the d
   // slices spread the gate/up work over the grid and h is formed from
-  // their partial sums between two grid barriers.
+  // their partial sums between two grid barriers. With more tiles than
+  // workgroups, the path whose busiest workgroup streams fewer stages wins,
+  // the sliced one paying kSliceCost stages for its h phase and second
+  // barrier (a few tiles past the grid would otherwise double the phase).
+  const int G = int(gridDim.x);
   const int up_tiles = nact * ((p.I + kStripCols - 1) / kStripCols);
-  if (5 * up_tiles >= 3 * int(gridDim.x)) {
+  bool whole;
+  if (up_tiles <= G) {
+    whole = 5 * up_tiles >= 3 * G;
+  } else {
+    const int whole_span = ((up_tiles + G - 1) / G) * ((p.d + kBK - 1) / kBK);
+    const int sliced_span = ((up_tiles * p.slices + G - 1) / G) * (p.slice_rows / kBK) + kSliceCost;
+    whole = p.slices == 1 || whole_span <= sliced_span;
+  }
+  if (whole) {
     p.slices = 1;
     p.slice_rows = p.d;
   }
