@@ -116,6 +116,25 @@ __device__ __forceinline__ float wave_sum(float v) {
   return __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(v), 63));
 }
 
+// Inclusive prefix sum over the wave: within each row of 16 lanes by
+// shifts of 1, 2, 4 and 8 lanes (lanes shifted in from outside the row add
+// 0), then row 0's total into row 1 and row 2's into row 3 (row_bcast:15),
+// then rows 0-1's total into rows 2 and 3 (row_bcast:31).
+template <int CTRL, int ROWS>
+__device__ __forceinline__ int scan_step(int v) {
+  return v + int(dpp<CTRL, ROWS>(0u, uint32_t(v)));
+}
+
+__device__ __forceinline__ int wave_scan_incl(int v) {
+  v = scan_step<0x111, 0xF>(v);  // row_shr:1
+  v = scan_step<0x112, 0xF>(v);  // row_shr:2
+  v = scan_step<0x114, 0xF>(v);  // row_shr:4
+  v = scan_step<0x118, 0xF>(v);  // row_shr:8
+  v = scan_step<kDppBcast15, 0xA>(v);
+  v = scan_step<kDppBcast31, 0xC>(v);
+  return v;
+}
+
 template <int CTRL, int ROWS>
 __device__ __forceinline__ float fmax_step(float v) {
   return fmaxf(v, __uint_as_float(dpp<CTRL, ROWS>(__float_as_uint(v), __float_as_uint(v))));
@@ -620,16 +639,7 @@ __device__ __forceinline__ void select_block(
       lc += c[v];
       la += a[v];
     }
-    int ic = lc, ia = la;  // inclusive scans over lanes
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const int oc = __shfl_up(ic, off);
-      const int oa = __shfl_up(ia, off);
-      if (lane >= off) {
-        ic += oc;
-        ia += oa;
-      }
-    }
+    const int ic = wave_scan_incl(lc), ia = wave_scan_incl(la);  // inclusive scans over lanes
     int pc = ic - lc, pa = ia - la;
 #pragma unroll
     for (int v = 0; v < NV; ++v) {
