@@ -438,13 +438,20 @@ __device__ __forceinline__ void select_block(
         uint32_t key[NV];
 #pragma unroll
         for (int v = 0; v < NV; ++v) key[v] = (lane + 64 * v < E) ? ord_bits(L[ti][v]) : 0u;
-        int e = 0;
-        uint32_t kv = 0, top = 0;
-        const int n = wave_rank<NV>(key, k, 0, lane, e, kv, top);
+        uint32_t cand = 0;
+#pragma unroll
+        for (int v = 0; v < NV; ++v) cand |= uint32_t(key[v] != 0) << v;
+        // The token's top-k are kept (lane j holds pick j): the leading ones
+        // that fall inside the critical set start phase 3.
+        const int n = wave_rank<NV>(key, k, 0, lane, pick_e[ti], pick_key[ti], pick_top[ti]);
+#pragma unroll
+        for (int v = 0; v < NV; ++v) picked[ti] |= uint32_t(((cand >> v) & 1u) && key[v] == 0) << v;
+        pick_n[ti] = n;
         if (lane < n) {
-          const float gap = from_ord_bits(top) - from_ord_bits(kv);
+          const float gap = from_ord_bits(pick_top[ti]) - from_ord_bits(pick_key[ti]);
           int bin = 0;
           for (int i = 1; i < k; ++i) bin += gap >= float(i) * bin_w;
+          const int e = pick_e[ti];
           atomicAdd(&lscore[e], 1u << (k - 1 - bin));
           if (lane == 0) atomicOr(&lrank0[e >> 5], 1u << (e & 31));
         }
@@ -602,6 +609,20 @@ __device__ __forceinline__ void select_block(
     if (t < B) {
       uint32_t key[NV];
       const uint32_t *mask = kind == MOE_POLICY_HIER ? req_allowed[t / g] : allowed;
+      if (kind == MOE_POLICY_LYNX) {
+        // Only the leading picks inside the critical set are the first picks
+        // of the masked order; the later ones become candidates again.
+        const unsigned long long in =
+            __ballot(lane < pick_n[ti] && bit_of(mask, pick_e[ti]));
+        const int pre = int(__builtin_ctzll(~in));
+        for (int r = pre; r < pick_n[ti]; ++r) {
+          const int er = __builtin_amdgcn_readlane(pick_e[ti], r);
+#pragma unroll
+          for (int v = 0; v < NV; ++v)
+            if (lane + 64 * v == er) picked[ti] &= ~(1u << v);
+        }
+        pick_n[ti] = pre;
+      }
 #pragma unroll
       for (int v = 0; v < NV; ++v) {
         const int e = lane + 64 * v;
