@@ -848,18 +848,47 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_kernel(Params p,
   unsigned char *stages = lds;
   unsigned char *meta = lds + kS * S::kSlot;
 
-  // Routing lists into LDS, in one round of independent loads (entries past
-  // the active ones are never read), and the barrier release base.
+  // Routing lists into LDS and the barrier release base. Every load is issued
+  // before the first value is used, so that the lists cost one round trip to
+  // memory, not one per list, and no load or store sits behind a branch (the
+  // compiler would sink the load into it): buffer loads past a list's end
+  // return zero, every LDS entry of the lists is written (entries past the
+  // active ones are never read), and the offsets' last rounds clamp to entry
+  // kMaxE, which all their lanes then write with the same value.
+  constexpr int kOffRounds = (kMaxE + 1 + kThreads - 1) / kThreads;
+  constexpr int kActRounds = kMaxE / kThreads;
+  constexpr int kPairRounds = kMaxPairs / kThreads;
+  static_assert(kMaxE % kThreads == 0 && kMaxPairs % kThreads == 0, "list rounds");
+  const __amdgpu_buffer_rsrc_t r_off = make_rsrc(offsets, uint32_t(p.E + 1) * 4u);
+  const __amdgpu_buffer_rsrc_t r_act = make_rsrc(active, uint32_t(p.E) * 4u);
+  const __amdgpu_buffer_rsrc_t r_tok = make_rsrc(p.pair_token, uint32_t(p.P) * 4u);
+  const __amdgpu_buffer_rsrc_t r_slot = make_rsrc(p.pair_slot, uint32_t(p.P) * 4u);
   const uint32_t rel_base = release_base(p.sync);
   const int nact = n_active[0];
-  for (int i = threadIdx.x; i <= p.E; i += kThreads) {
-    reinterpret_cast<int16_t *>(meta + kMetaOff)[i] = int16_t(offsets[i]);
-    if (i < p.E) reinterpret_cast<int16_t *>(meta + kMetaAct)[i] = int16_t(active[i]);
+  int32_t offv[kOffRounds], actv[kActRounds], tokv[kPairRounds], slotv[kPairRounds];
+#pragma unroll
+  for (int r = 0; r < kOffRounds; ++r)
+    offv[r] = __builtin_amdgcn_raw_buffer_load_b32(r_off, min(int(threadIdx.x) + r * kThreads, kMaxE) * 4, 0, 0);
+#pragma unroll
+  for (int r = 0; r < kActRounds; ++r)
+    actv[r] = __builtin_amdgcn_raw_buffer_load_b32(r_act, (int(threadIdx.x) + r * kThreads) * 4, 0, 0);
+#pragma unroll
+  for (int r = 0; r < kPairRounds; ++r) {
+    const int o = (int(threadIdx.x) + r * kThreads) * 4;
+    tokv[r] = __builtin_amdgcn_raw_buffer_load_b32(r_tok, o, 0, 0);
+    slotv[r] = __builtin_amdgcn_raw_buffer_load_b32(r_slot, o, 0, 0);
   }
-  for (int i = threadIdx.x; i < p.P; i += kThreads) {
-    const int t = p.pair_token[i];
-    meta[kMetaTok + i] = uint8_t(t);
-    reinterpret_cast<int16_t *>(meta + kMetaRow)[i] = int16_t(t * p.k + p.pair_slot[i]);
+#pragma unroll
+  for (int r = 0; r < kOffRounds; ++r)
+    reinterpret_cast<int16_t *>(meta + kMetaOff)[min(int(threadIdx.x) + r * kThreads, kMaxE)] = int16_t(offv[r]);
+#pragma unroll
+  for (int r = 0; r < kActRounds; ++r)
+    reinterpret_cast<int16_t *>(meta + kMetaAct)[threadIdx.x + r * kThreads] = int16_t(actv[r]);
+#pragma unroll
+  for (int r = 0; r < kPairRounds; ++r) {
+    const int i = int(threadIdx.x) + r * kThreads;
+    meta[kMetaTok + i] = uint8_t(tokv[r]);
+    reinterpret_cast<int16_t *>(meta + kMetaRow)[i] = int16_t(tokv[r] * p.k + slotv[r]);
   }
   uint32_t *fill = reinterpret_cast<uint32_t *>(meta + kMetaFill);
   for (int t = threadIdx.x; t < p.B; t += kThreads) fill[t] = 0;
