@@ -20,13 +20,13 @@
 //             largest probability in S (0 while t has fewer than k there);
 //             ties to the lower index.
 //   HIER(m, m_r, g)  "XShare", summary and abstract (hierarchical selection
-//             for speculative batches; the steps are this build's reading):
+//             for speculative batches; the steps are the reading taken here):
 //             the batch keeps the BUDGET(m) set; request r (tokens r*g ..
 //             r*g+g-1) keeps the m_r experts of that set with the largest
 //             mass summed over its own tokens, in token order (ties to the
 //             lower index); its tokens rank inside that request set.
 //   LYNX(m)   "Lynx", Technical Summary 2.1 and 2.2 (the constants are
-//             this build's reading): the gap between a token's rank-0 logit
+//             the reading taken here): the gap between a token's rank-0 logit
 //             and each of its top-k logits (float32) falls into one of k
 //             bins of width bin_w = ln(E/k) (bin = number of i in 1..k-1 with
 //             gap >= i * bin_w, float32 products); an expert scores

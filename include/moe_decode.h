@@ -34,10 +34,10 @@
  *                              each token takes its top min(k, m_r) inside
  *                              its request's set ("XShare", summary and
  *                              abstract: hierarchical selection for
- *                              speculative decoding; this build's reading).
+ *                              speculative decoding; the reading taken here).
  *                   LYNX(m)    confidence-gated remap ("Lynx", Technical
- *                              Summary 2.1 and 2.2; constants are this
- *                              build's reading): the gap between a token's
+ *                              Summary 2.1 and 2.2; constants are the
+ *                              reading taken here): the gap between a token's
  *                              rank-0 logit and each of its top-k logits is
  *                              binned into k bins of width ln(E/k) (float32);
  *                              an expert scores 2^(k-1-bin) per (token, rank

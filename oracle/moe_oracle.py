@@ -55,7 +55,7 @@ Readings where the pages are silent (each is stated where it is used):
   R9  lynx(m), a confidence-gated remap ([Lynx] section 2.1 "Token
       Confidence" and "Expert Rank Hierarchy", section 2.2 "Confidence
       Analyzer", "Adaptive Expert Scorer", "Expert Remapper"; the page gives
-      no formulas, so every constant below is this build's reading):
+      no formulas, so every constant below is the reading taken here):
       * confidence of token t's rank-j expert (j < k) is the logit gap
         delta = L[t, rank 0] - L[t, rank j] (float32 subtraction);
       * AffinityBinning: k bins of width w = ln(E / k) (the inverse sparsity
