@@ -257,6 +257,13 @@ struct Params {
   int n_dstrips;              // 128-column strips of d
 };
 
+// By active-expert count: gate/up stages of kBK rows per d slice (all of d
+// for whole tiles). A kernel argument of its own, never written, so that the
+// kernel reads the entry it needs from the argument segment.
+struct UpPlan {
+  uint32_t blk4[(kMaxE + 1 + 3) / 4];  // entry n in byte n % 4 of word n / 4
+};
+
 // A position in a workgroup's stage sequence. The workgroup's items are
 // b, b+G, b+2G, ... of one list: gate/up items first (expert, 64-column strip
 // of I, slice of d), then down items (expert, 128-column strip of d, all of
@@ -837,7 +844,7 @@ __device__ __forceinline__ void change_to_down(const Params &p, const Stream<MTX
 // The first down stages' weights are in flight while the workgroup waits at
 // the grid barriers; their A tiles are copied once h is complete.
 template <int MTX>
-__global__ __launch_bounds__(kThreads, 1) void ffn_kernel(Params p,
+__global__ __launch_bounds__(kThreads, 1) void ffn_kernel(Params p, const UpPlan up,
                                                           const int32_t *__restrict__ n_active,
                                                           const int32_t *__restrict__ active,
                                                           const int32_t *__restrict__ offsets) {
@@ -906,27 +913,13 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_kernel(Params p,
   __syncthreads();
   zero_empty_groups(p, meta);
 
-  // Whole-d gate/up tiles when the active experts' tiles (expert x 64-column
-  // strip of I) fill enough of the grid to keep HBM busy: each tile then
-  // forms its h columns itself and the grid meets once. Otherwise the d
-  // slices spread the gate/up work over the grid and h is formed from
-  // their partial sums between two grid barriers. With more tiles than
-  // workgroups, the path whose busiest workgroup streams fewer stages wins,
-  // the sliced one paying kSliceCost stages for its h phase and second
-  // barrier (a few tiles past the grid would otherwise double the phase).
-  const int G = int(gridDim.x);
-  const int up_tiles = nact * ((p.I + kStripCols - 1) / kStripCols);
-  bool whole;
-  if (up_tiles <= G) {
-    whole = 5 * up_tiles >= 3 * G;
-  } else {
-    const int whole_span = ((up_tiles + G - 1) / G) * ((p.d + kBK - 1) / kBK);
-    const int sliced_span = ((up_tiles * p.slices + G - 1) / G) * (p.slice_rows / kBK) + kSliceCost;
-    whole = p.slices == 1 || whole_span <= sliced_span;
-  }
-  if (whole) {
-    p.slices = 1;
-    p.slice_rows = p.d;
+  // The gate/up split for this many active experts, chosen on the host
+  // (plan_gate_up): stages of kBK rows per d slice, all of d for whole tiles.
+  {
+    const int blk = int((up.blk4[nact >> 2] >> (8 * (nact & 3))) & 0xFFu);
+    const int nblk = (p.d + kBK - 1) / kBK;
+    p.slices = (nblk + blk - 1) / blk;
+    p.slice_rows = p.slices == 1 ? p.d : blk * kBK;
   }
 
   const Stream<MTX> st(p, lds_addr(meta));
@@ -1105,9 +1098,54 @@ int device_cus() {
   return cus;
 }
 
+// Gate/up split for every possible active-expert count n (the count is only
+// known on the device). A gate/up tile is (active expert, 64-column strip of
+// I). Whole-d tiles when the tiles fill enough of the grid to keep HBM busy:
+// each tile then forms its h columns itself and the grid meets once.
+// Otherwise slices of d spread the gate/up work over the grid and h is
+// formed from their partial sums between two grid barriers. With more tiles
+// than workgroups, the path whose busiest workgroup streams fewer stages
+// wins, the sliced one paying kSliceCost stages for its h phase and second
+// barrier (a few tiles past the grid would otherwise double the phase). A
+// sliced split takes the slice count, 2 up to the planned one (whose partial
+// sums the workspace holds), whose busiest workgroup streams the fewest
+// stages, ties to more slices (72 tiles: 3 slices of 6 stages make 216 items,
+// where 4 slices of 4 make 288, two rounds of 4 for some workgroups).
+static_assert(kMaxDim / kBK <= 255, "stages per slice fit a byte");
+void plan_gate_up(const Params &p, int G, UpPlan &up) {
+  for (uint32_t &w : up.blk4) w = 0;
+  const int nblk = ceil_div(p.d, kBK);
+  const int strips = ceil_div(p.I, kStripCols);
+  const int planned = p.slices, planned_blk = p.slice_rows / kBK;
+  for (int n = 0; n <= p.E; ++n) {
+    const int tiles = n * strips;
+    bool whole;
+    if (tiles <= G) {
+      whole = 5 * tiles >= 3 * G;
+    } else {
+      const int whole_span = ceil_div(tiles, G) * nblk;
+      const int sliced_span = ceil_div(tiles * planned, G) * planned_blk + kSliceCost;
+      whole = planned == 1 || whole_span <= sliced_span;
+    }
+    int blk = nblk;
+    if (!whole) {
+      int best_span = 0x7fffffff;
+      for (int sl = 2; sl <= planned; ++sl) {
+        const int b = ceil_div(nblk, sl);
+        const int span = ceil_div(tiles * ceil_div(nblk, b), G) * b;
+        if (span <= best_span) {
+          best_span = span;
+          blk = b;
+        }
+      }
+    }
+    up.blk4[n >> 2] |= uint32_t(blk) << (8 * (n & 3));
+  }
+}
+
 template <int MTX>
-void launch_ffn(int grid, const Params &p, const moe_routing_t &r, hipStream_t s) {
-  ffn_kernel<MTX><<<grid, kThreads, 0, s>>>(p, r.n_active, r.active_experts, r.expert_offsets);
+void launch_ffn(int grid, const Params &p, const UpPlan &up, const moe_routing_t &r, hipStream_t s) {
+  ffn_kernel<MTX><<<grid, kThreads, 0, s>>>(p, up, r.n_active, r.active_experts, r.expert_offsets);
 }
 
 }  // namespace
@@ -1150,14 +1188,16 @@ hipError_t launch_expert_ffn(const void *x, const void *w_gate, const void *w_up
     const int items = max_active * (ceil_div(I, kStripCols) * plan.up_slices + ceil_div(d, 2 * kStripCols));
     const int cus = device_cus();
     const int grid = items < cus ? items : cus;
+    UpPlan up;
+    plan_gate_up(p, grid, up);
     // An expert has at most B tokens: A tiles of 16 * MTX rows cover them
     // (experts with more than 64 tokens take several passes).
     if (B <= 16)
-      launch_ffn<1>(grid, p, r, s);
+      launch_ffn<1>(grid, p, up, r, s);
     else if (B <= 32)
-      launch_ffn<2>(grid, p, r, s);
+      launch_ffn<2>(grid, p, up, r, s);
     else
-      launch_ffn<4>(grid, p, r, s);
+      launch_ffn<4>(grid, p, up, r, s);
   } else {
     float *h = reinterpret_cast<float *>(ws + plan.h);
     up_f32_kernel<<<dim3(ceil_div(I, kF32Cols), P), kF32Threads, 0, s>>>(
