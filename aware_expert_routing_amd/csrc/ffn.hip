@@ -1109,36 +1109,35 @@ int device_cus() {
 // barrier (a few tiles past the grid would otherwise double the phase). A
 // sliced split takes the slice count, 2 up to the planned one (whose partial
 // sums the workspace holds), whose busiest workgroup streams the fewest
-// stages, ties to more slices (72 tiles: 3 slices of 6 stages make 216 items,
-// where 4 slices of 4 make 288, two rounds of 4 for some workgroups).
+// stages, ties to fewer slices (fewer, longer items and fewer partial sums
+// to add: measured faster at 8-9 active experts). 72 tiles: 3 slices of 6
+// stages make 216 items, where 4 slices of 4 make 288, two rounds of 4 for
+// some workgroups.
 static_assert(kMaxDim / kBK <= 255, "stages per slice fit a byte");
 void plan_gate_up(const Params &p, int G, UpPlan &up) {
   for (uint32_t &w : up.blk4) w = 0;
   const int nblk = ceil_div(p.d, kBK);
   const int strips = ceil_div(p.I, kStripCols);
-  const int planned = p.slices, planned_blk = p.slice_rows / kBK;
+  const int planned = p.slices;
   for (int n = 0; n <= p.E; ++n) {
     const int tiles = n * strips;
-    bool whole;
-    if (tiles <= G) {
-      whole = 5 * tiles >= 3 * G;
-    } else {
-      const int whole_span = ceil_div(tiles, G) * nblk;
-      const int sliced_span = ceil_div(tiles * planned, G) * planned_blk + kSliceCost;
-      whole = planned == 1 || whole_span <= sliced_span;
-    }
-    int blk = nblk;
-    if (!whole) {
-      int best_span = 0x7fffffff;
-      for (int sl = 2; sl <= planned; ++sl) {
-        const int b = ceil_div(nblk, sl);
-        const int span = ceil_div(tiles * ceil_div(nblk, b), G) * b;
-        if (span <= best_span) {
-          best_span = span;
-          blk = b;
-        }
+    int best_blk = nblk, best_span = 0x7fffffff;
+    for (int sl = 2; sl <= planned; ++sl) {
+      const int b = ceil_div(nblk, sl);
+      const int span = ceil_div(tiles * ceil_div(nblk, b), G) * b;
+      if (span < best_span) {
+        best_span = span;
+        best_blk = b;
       }
     }
+    bool whole;
+    if (planned == 1)
+      whole = true;
+    else if (tiles <= G)
+      whole = 5 * tiles >= 3 * G;
+    else
+      whole = ceil_div(tiles, G) * nblk <= best_span + kSliceCost;
+    const int blk = whole ? nblk : best_blk;
     up.blk4[n >> 2] |= uint32_t(blk) << (8 * (n & 3));
   }
 }
