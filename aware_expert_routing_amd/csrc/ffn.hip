@@ -261,7 +261,7 @@ struct Params {
 // for whole tiles). A kernel argument of its own, never written, so that the
 // kernel reads the entry it needs from the argument segment.
 struct UpPlan {
-  uint32_t blk4[(kMaxE + 1 + 3) / 4];  // entry n in byte n % 4 of word n / 4
+  uint32_t e2[(kMaxE + 2) / 2];  // entry n in half n % 2 of word n / 2: stages per slice | slices << 8
 };
 
 // A position in a workgroup's stage sequence. The workgroup's items are
@@ -915,11 +915,27 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_kernel(Params p, const UpPlan
 
   // The gate/up split for this many active experts, chosen on the host
   // (plan_gate_up): stages of kBK rows per d slice, all of d for whole tiles.
-  {
-    const int blk = int((up.blk4[nact >> 2] >> (8 * (nact & 3))) & 0xFFu);
-    const int nblk = (p.d + kBK - 1) / kBK;
-    p.slices = (nblk + blk - 1) / blk;
-    p.slice_rows = p.slices == 1 ? p.d : blk * kBK;
+  if constexpr (MTX < 4) {
+    const uint32_t e = (up.e2[nact >> 1] >> (16 * (nact & 1))) & 0xFFFFu;
+    p.slices = int(e >> 8);
+    p.slice_rows = p.slices == 1 ? p.d : int(e & 0xFFu) * kBK;
+  } else {
+    // 64-token passes: the same rule with the planned slices, decided here
+    // (reading the table slowed this instantiation's stage loop by 4-6%).
+    const int G = int(gridDim.x);
+    const int up_tiles = nact * ((p.I + kStripCols - 1) / kStripCols);
+    bool whole;
+    if (up_tiles <= G) {
+      whole = 5 * up_tiles >= 3 * G;
+    } else {
+      const int whole_span = ((up_tiles + G - 1) / G) * ((p.d + kBK - 1) / kBK);
+      const int sliced_span = ((up_tiles * p.slices + G - 1) / G) * (p.slice_rows / kBK) + kSliceCost;
+      whole = p.slices == 1 || whole_span <= sliced_span;
+    }
+    if (whole) {
+      p.slices = 1;
+      p.slice_rows = p.d;
+    }
   }
 
   const Stream<MTX> st(p, lds_addr(meta));
@@ -1115,7 +1131,7 @@ int device_cus() {
 // some workgroups.
 static_assert(kMaxDim / kBK <= 255, "stages per slice fit a byte");
 void plan_gate_up(const Params &p, int G, UpPlan &up) {
-  for (uint32_t &w : up.blk4) w = 0;
+  for (uint32_t &w : up.e2) w = 0;
   const int nblk = ceil_div(p.d, kBK);
   const int strips = ceil_div(p.I, kStripCols);
   const int planned = p.slices;
@@ -1138,7 +1154,8 @@ void plan_gate_up(const Params &p, int G, UpPlan &up) {
     else
       whole = ceil_div(tiles, G) * nblk <= best_span + kSliceCost;
     const int blk = whole ? nblk : best_blk;
-    up.blk4[n >> 2] |= uint32_t(blk) << (8 * (n & 3));
+    const int slices = ceil_div(nblk, blk);
+    up.e2[n >> 1] |= (uint32_t(blk) | uint32_t(slices) << 8) << (16 * (n & 1));
   }
 }
 
