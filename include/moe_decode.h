@@ -146,8 +146,8 @@ typedef struct {
  * The workspace must be zero-filled once, before its first use (e.g.
  * hipMemset after allocation); afterwards the caller must not write it. Its
  * first bytes hold the synchronisation words of the bf16 expert FFN (grid
- * barrier, per-token counters), which every call leaves ready for the next
- * one. The same workspace may serve
+ * barrier, a counter per output column strip and 16-token group), which
+ * every call leaves ready for the next one. The same workspace may serve
  * consecutive calls on one stream; calls that may overlap need separate
  * workspaces. The bf16 expert FFN runs one workgroup per compute unit and
  * needs all of them resident together: do not run it next to another kernel
