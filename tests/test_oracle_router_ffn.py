@@ -206,3 +206,51 @@ def test_oea_reduces_active_experts_on_skewed_workload():
     assert n[8] == n_topk
     assert all(n[a] <= n[a + 1] for a in range(1, 8))
     assert n[2] < n_topk
+
+
+def test_slot_weights_pair_with_their_experts_hand_worked():
+    """Two experts with the same gate/up and different down projections, one
+    token, k = 2. x = (1, 0), W_g puts logit ln 3 on expert 0 and 0 on expert
+    1, so the renormalised weights are 3/4 and 1/4. Both experts have
+    x G = 2 and x U = 1, so h = SiLU(2); D_0 = [1, 0] and D_1 = [0, 1] route
+    h to different output columns. y = SiLU(2) * (3/4, 1/4): each weight must
+    multiply its own expert's output."""
+    x = np.array([[1.0, 0.0]], dtype=np.float32)
+    wg = np.array([[math.log(3.0), 0.0], [0.0, 0.0]], dtype=np.float32)
+    G = np.array([[[2.0], [0.0]]] * 2, dtype=np.float32)
+    U = np.array([[[1.0], [0.0]]] * 2, dtype=np.float32)
+    D = np.array([[[1.0, 0.0]], [[0.0, 1.0]]], dtype=np.float32)
+    out = orc.moe_layer(x, wg, None, G, U, D, "f32", "topk", k=2)
+    assert out["ids"].tolist() == [[0, 1]]
+    s2 = 2 * (1 + math.tanh(1.0)) / 2  # SiLU(2) = 2 / (1 + e^-2)
+    # ln 3 rounded to float32 moves the weights by about 1e-8
+    np.testing.assert_allclose(out["y"][0], [0.75 * s2, 0.25 * s2], rtol=1e-7)
+
+
+@pytest.mark.parametrize("policy,kw", [("topk", {}), ("oea", {"k0": 1}), ("budget", {"m": 4}),
+                                       ("greedy", {"m": 3})])
+def test_slot_weights_pair_with_their_experts(policy, kw):
+    """Experts that share G and U and whose down projections are D scaled by
+    2^e: expert e computes 2^e f(x) with f one dense SwiGLU. So
+    y[t] = (sum_j w[t,j] 2^{e_j}) f(x_t), where w is the softmax of the
+    selected logits computed here with scipy. Distinct logits give distinct
+    weights and distinct scales, so a weight paired with another slot's
+    expert changes the factor."""
+    from scipy.special import softmax as sp_softmax
+    E, B, k = 6, 5, 3
+    x, wg, G, U, D = _tiny(E=E, B=B)
+    G[:] = G[0]
+    U[:] = U[0]
+    D = np.stack([D[0] * np.float32(2.0 ** e) for e in range(E)]).astype(np.float32)
+    out = orc.moe_layer(x, wg, None, G, U, D, "f32", policy, k=k, **kw)
+    f = _dense_swiglu(x.astype(np.float64), G[0].astype(np.float64), U[0].astype(np.float64),
+                      D[0].astype(np.float64))
+    L32 = out["logits32"]
+    for t in range(B):
+        sel = [int(e) for e in out["ids"][t] if e >= 0]
+        assert len(sel) >= 2, "the pin needs tokens with several experts"
+        p = sp_softmax(L32[t].astype(np.float64))[sel]
+        w = p / p.sum()
+        assert len(set(np.round(w, 12))) == len(w), "weights must be distinct"
+        c = float(np.dot(w, [2.0 ** e for e in sel]))
+        np.testing.assert_allclose(out["y"][t], c * f[t], rtol=1e-11, atol=1e-13)
