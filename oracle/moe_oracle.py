@@ -248,7 +248,8 @@ def select_budget(L32: np.ndarray, k: int, m: int, mass=None) -> np.ndarray:
     return _ids_matrix([_first_in(token_order(l), S, k) for l in L32], k)
 
 
-def greedy_retained_set(L32: np.ndarray, k: int, m: int) -> np.ndarray:
+def greedy_retained_set(L32: np.ndarray, k: int, m: int, prefer=None,
+                        term_rel: float = 0.0) -> np.ndarray:
     """Greedy maximisation of the retained top-k gating mass
     F(S) = sum_t (sum of token t's k largest probabilities inside S), one
     expert at a time ([XShare] abstract: batch-aware selection solved
@@ -256,12 +257,30 @@ def greedy_retained_set(L32: np.ndarray, k: int, m: int) -> np.ndarray:
     on float32-rounded values, ties to the lower index (reading R2).
     Boolean mask [E].
 
-    Pinned by: brute force on tiny inputs (1 - 1/e bound), and equality with
-    budget(m) when m <= k (F is then modular on |S| <= k).
+    Near ties. An implementation that computes the probabilities and gains
+    in float32 can order two gains that differ only by rounding the other
+    way, and both greedy runs are then correct (the reading taken for budget's
+    mass near-ties). Given ``prefer`` (boolean [E], the set such an
+    implementation chose) and ``term_rel`` (a bound on the relative error of
+    each of its float32 probabilities), a round whose best candidate is not in
+    ``prefer`` takes instead the lowest-index candidate in ``prefer`` whose
+    gain is within the rounding bound of the best. The bound of candidate e is
+    term_rel' * sum over tokens with p_t[e] >= thr_t / 2 of (p_t[e] + thr_t)
+    (the error of each term max(0, p_t[e] - thr_t), term_rel' = term_rel +
+    2^-24 for the subtraction; tokens further below their threshold add 0 on
+    both sides) plus (B - 1) 2^-24 gain_e (a float32 sum of B terms), where
+    thr_t is token t's k-th largest probability inside S (0 while S holds
+    fewer than k). Two gains are near-tied when they differ by at most the
+    sum of their bounds. Without ``prefer`` the run is the exact greedy.
+
+    Pinned by: hand-worked examples (greedy differs from budget(m) and from
+    the exhaustive optimum), brute force on tiny inputs (1 - 1/e bound), and
+    equality with budget(m) when m <= k (F is then modular on |S| <= k).
     """
     B, E = L32.shape
     P = np.stack([softmax_row(np.asarray(l, np.float32).astype(np.float64)) for l in L32])
     S = np.zeros(E, dtype=bool)
+    u = 2.0 ** -24
 
     def F(mask):
         tot = 0.0
@@ -270,24 +289,50 @@ def greedy_retained_set(L32: np.ndarray, k: int, m: int) -> np.ndarray:
             tot += v.sum()
         return tot
 
+    def thresholds(mask):
+        thr = np.zeros(B)
+        for t in range(B):
+            v = np.sort(P[t][mask])[::-1]
+            if v.shape[0] >= k:
+                thr[t] = v[k - 1]
+        return thr
+
     base = 0.0
     for _ in range(m):
         best_e, best_gain = -1, None
+        gains = {}
         for e in range(E):
             if S[e]:
                 continue
             S[e] = True
             gain = np.float32(F(S) - base)
             S[e] = False
+            gains[e] = float(gain)
             if best_gain is None or gain > best_gain:
                 best_e, best_gain = e, gain
+        if prefer is not None and not prefer[best_e]:
+            thr = thresholds(S)
+            rel = term_rel + u
+
+            def bound(e):
+                near = P[:, e] >= thr / 2
+                return rel * float(np.sum((P[:, e] + thr)[near])) + (B - 1) * u * gains[e]
+
+            tb = bound(best_e)
+            for e in sorted(gains):
+                if prefer[e] and gains[best_e] - gains[e] <= tb + bound(e):
+                    best_e = e
+                    break
         S[best_e] = True
         base = F(S)
     return S
 
 
-def select_greedy(L32: np.ndarray, k: int, m: int) -> np.ndarray:
-    S = greedy_retained_set(L32, k, m)
+def select_greedy(L32: np.ndarray, k: int, m: int, prefer=None, term_rel: float = 0.0) -> np.ndarray:
+    """greedy(m): each token takes the first min(k, m) experts of its own
+    order inside the greedy set. ids [B, k], -1 padded. ``prefer`` and
+    ``term_rel`` as in greedy_retained_set."""
+    S = greedy_retained_set(L32, k, m, prefer, term_rel)
     return _ids_matrix([_first_in(token_order(l), S, k) for l in L32], k)
 
 

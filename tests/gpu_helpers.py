@@ -87,6 +87,53 @@ def routing_numpy(r: L.Routing) -> dict:
     return out
 
 
+F32_U = 2.0 ** -24  # unit roundoff of float32
+
+
+def softmax_term_rel(L32: np.ndarray) -> np.ndarray:
+    """Bound on the relative error of each float32 probability
+    p[t,e] = expf(l - mx) / sum the selection kernel forms, [B, E]:
+      - l - mx rounded: absolute error <= u |l - mx|, which exp turns into a
+        relative error of the same size;
+      - expf: at most 2 ulp (4u relative) for the numerator and for every
+        term of the sum;
+      - the sum: its terms' errors average to u * H_t + 4u with
+        H_t = sum_e p[t,e] |l - mx| (p-weighted), plus (NV - 1) + 6 roundings
+        (NV = ceil(E/64) serial adds per lane, then a 6-level wave tree);
+      - the division: u.
+    Total: u (|l - mx| + H_t + 14 + NV)."""
+    L = np.asarray(L32, dtype=np.float64)
+    B, E = L.shape
+    nv = -(-E // 64)
+    gap = L.max(axis=1, keepdims=True) - L
+    P = np.exp(-gap)
+    P /= P.sum(axis=1, keepdims=True)
+    H = (P * gap).sum(axis=1, keepdims=True)
+    return F32_U * (gap + H + 14 + nv)
+
+
+def batch_mass_tolerance(L32: np.ndarray) -> np.ndarray:
+    """Per-expert bound on |M_gpu - M_exact| for the budget masses
+    M[e] = sum_t p[t,e] that the kernel adds in float32 in token order:
+    sum_t p[t,e] * softmax_term_rel[t,e] for the terms, plus (B - 1) u M[e]
+    for the B - 1 roundings of the running sum (each at most u times a
+    partial sum, itself at most M[e]). [E]."""
+    L = np.asarray(L32, dtype=np.float64)
+    B = L.shape[0]
+    P = np.exp(L - L.max(axis=1, keepdims=True))
+    P /= P.sum(axis=1, keepdims=True)
+    M = P.sum(axis=0)
+    return (P * softmax_term_rel(L32)).sum(axis=0) + (B - 1) * F32_U * M
+
+
+def assert_batch_mass_close(Mg: np.ndarray, Mref: np.ndarray, L32: np.ndarray, tag: str = ""):
+    tol = batch_mass_tolerance(L32)
+    err = np.abs(np.asarray(Mg, np.float64) - Mref)
+    bad = err > tol
+    assert not bad.any(), (f"{tag} batch_mass: {int(bad.sum())} experts beyond the float32 bound "
+                           f"(worst err/bound {float((err / tol).max()):.2f})")
+
+
 def weight_rtol_from_logits(Lg: np.ndarray, Lref: np.ndarray) -> np.ndarray:
     """Per-token relative tolerance of the gate weights when the two sides
     rank different float32 logits. With every selected logit off by at most

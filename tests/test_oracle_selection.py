@@ -496,3 +496,38 @@ def test_lynx_argument_checks():
         orc.select_lynx(L, 4, 3)    # m < k: exactly k per token impossible
     with pytest.raises(ValueError):
         orc.select_lynx(L, 4, 17)   # m > E
+
+
+# ------------------------------------------------ greedy near-tie acceptance
+
+def _ln_logits(rows):
+    return np.array([[math.log(p) for p in r] for r in rows], dtype=np.float32)
+
+
+def test_greedy_prefer_accepts_exact_tie_only():
+    """Round 2 below ties exactly: t0 p = (.5, .3, .2), t1 p = (.5, .2, .3),
+    k = 1; after e0 neither e1 nor e2 beats a token's 0.5, so both gains are
+    0. Exact greedy takes the lower index; a preferred e2 is accepted."""
+    L = _ln_logits([[.5, .3, .2], [.5, .2, .3]])
+    assert np.flatnonzero(orc.greedy_retained_set(L, 1, 2)).tolist() == [0, 1]
+    pref = np.array([True, False, True])
+    assert np.flatnonzero(orc.greedy_retained_set(L, 1, 2, prefer=pref)).tolist() == [0, 2]
+
+
+def test_greedy_prefer_rejects_a_clear_loser():
+    """greedy_coverage_k1 of the golden file: round 2's gains are 0.5 (e2)
+    and 0.2 (e1), far apart compared with float32 rounding, so a preferred
+    {0, 1} (budget's set) is not accepted even at a generous term error."""
+    L = _ln_logits([[.6, .3, .1], [.6, .3, .1], [.1, .3, .6]])
+    pref = np.array([True, True, False])
+    S = orc.greedy_retained_set(L, 1, 2, prefer=pref, term_rel=1e-4)
+    assert np.flatnonzero(S).tolist() == [0, 2]
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_greedy_prefer_own_set_is_unchanged(seed):
+    L = make_logits(8, 32, seed=seed)
+    for m in (3, 8, 17):
+        S = orc.greedy_retained_set(L, 4, m)
+        S2 = orc.greedy_retained_set(L, 4, m, prefer=S.copy(), term_rel=1e-5)
+        assert np.array_equal(S, S2)
