@@ -19,6 +19,9 @@ MOE_ERR_INVALID_ARG = 1
 MOE_ERR_UNSUPPORTED = 2
 MOE_ERR_WORKSPACE = 3
 MOE_ERR_HIP = 4
+MOE_ERR_RESIDENCY = 5
+MOE_ERR_SYNC_TIMEOUT = 6
+MOE_WS_STATUS_BYTES = 512
 
 MOE_F32 = 0
 MOE_BF16 = 1
@@ -30,8 +33,8 @@ MOE_POLICY_GREEDY = 3
 MOE_POLICY_HIER = 4
 MOE_POLICY_LYNX = 5
 
-EXPORTS = ("moe_workspace_bytes", "moe_route", "moe_select", "moe_expert_ffn",
-           "moe_layer_decode", "moe_status_string", "moe_read_stream")
+EXPORTS = ("moe_workspace_bytes", "moe_workspace_check", "moe_route", "moe_select",
+           "moe_expert_ffn", "moe_layer_decode", "moe_status_string", "moe_read_stream")
 
 
 class MoeError(RuntimeError):
@@ -80,6 +83,8 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
                                      Policy, vp, ctypes.POINTER(RoutingC), vp, vp, sz, vp]
     lib.moe_status_string.restype = ctypes.c_char_p
     lib.moe_status_string.argtypes = [c_int]
+    lib.moe_workspace_check.restype = c_int
+    lib.moe_workspace_check.argtypes = [vp, sz]
     lib.moe_read_stream.restype = c_int
     lib.moe_read_stream.argtypes = [vp, sz, vp, vp]
     if path is None:
@@ -171,6 +176,21 @@ def alloc_workspace(B: int, d: int, E: int, I: int, k: int, dtype, device="cuda"
         raise MoeError(MOE_ERR_UNSUPPORTED, status_string(MOE_ERR_UNSUPPORTED))
     # Zero-filled once: the expert FFN keeps its grid-barrier words here.
     return torch.zeros((n,), dtype=torch.uint8, device=device)
+
+
+def workspace_status(workspace_head: bytes) -> int:
+    """moe_workspace_check on a host copy of a workspace's first
+    MOE_WS_STATUS_BYTES bytes; returns the status code."""
+    buf = ctypes.create_string_buffer(bytes(workspace_head), len(workspace_head))
+    return int(load().moe_workspace_check(ctypes.cast(buf, ctypes.c_void_p), len(workspace_head)))
+
+
+def check_workspace(workspace) -> None:
+    """Copies the status bytes of a device workspace (waiting for the
+    current stream) and raises MoeError if a grid-wide wait of the expert FFN
+    gave up in any call since the workspace was zero-filled."""
+    head = workspace[:MOE_WS_STATUS_BYTES].cpu().numpy().tobytes()
+    _check(workspace_status(head))
 
 
 def moe_route(x, w_g, bias, logits, workspace, stream=None):

@@ -1,6 +1,7 @@
 // extern "C" entry points of libmoe_decode: argument checks (before any HIP
 // call), workspace planning and kernel launches on the caller's stream.
 #include <stdint.h>
+#include <string.h>
 
 #include "moe_internal.h"
 
@@ -77,7 +78,10 @@ size_t route_bytes(int B, int d, int E) {
     if (st_ != MOE_OK) return st_;        \
   } while (0)
 
-moe_status_t hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+moe_status_t hip_status(hipError_t e) {
+  if (e == hipSuccess) return MOE_OK;
+  return e == hipErrorCooperativeLaunchTooLarge ? MOE_ERR_RESIDENCY : MOE_ERR_HIP;
+}
 
 }  // namespace
 
@@ -154,6 +158,7 @@ moe_status_t moe_layer_decode(const void *x, const void *w_g, const float *bias,
   MOE_TRY(check_routing(routing, policy.kind == MOE_POLICY_BUDGET || policy.kind == MOE_POLICY_HIER));
   const Workspace plan = plan_workspace(B, d, E, I, policy.k, dt);
   MOE_TRY(check_workspace(workspace, workspace_bytes, plan.total));
+  MOE_TRY(hip_status(expert_ffn_launchable(dt, B, d, E, I, policy.k, plan)));
   hipStream_t s = static_cast<hipStream_t>(stream);
   char *ws = static_cast<char *>(workspace);
   if (dt == MOE_BF16) {
@@ -168,6 +173,13 @@ moe_status_t moe_layer_decode(const void *x, const void *w_g, const float *bias,
   }
   return hip_status(launch_expert_ffn(x, w_gate, w_up, w_down, dt, B, d, E, I, policy.k, *routing,
                                       y, ws, plan, s));
+}
+
+moe_status_t moe_workspace_check(const void *status_host, size_t bytes) {
+  if (!status_host || bytes < MOE_WS_STATUS_BYTES) return MOE_ERR_INVALID_ARG;
+  uint32_t word;
+  memcpy(&word, static_cast<const char *>(status_host) + kSyncErrOffset, sizeof(word));
+  return word != 0 ? MOE_ERR_SYNC_TIMEOUT : MOE_OK;
 }
 
 moe_status_t moe_read_stream(const void *src, size_t bytes, uint32_t *out, void *stream) {
@@ -188,6 +200,11 @@ const char *moe_status_string(moe_status_t status) {
       return "MOE_ERR_WORKSPACE: workspace missing, misaligned or too small";
     case MOE_ERR_HIP:
       return "MOE_ERR_HIP: a kernel launch failed";
+    case MOE_ERR_RESIDENCY:
+      return "MOE_ERR_RESIDENCY: the expert FFN's workgroups cannot all be resident on this device";
+    case MOE_ERR_SYNC_TIMEOUT:
+      return "MOE_ERR_SYNC_TIMEOUT: a grid-wide wait of the expert FFN gave up; outputs of the calls "
+             "since the workspace was zero-filled are unspecified";
     default:
       return "unknown moe_status_t";
   }

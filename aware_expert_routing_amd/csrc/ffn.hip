@@ -29,6 +29,8 @@
 //     for the group's tokens, adding the slots in order (no float atomics:
 //     results are reproducible).
 // float32 path (small layers): plain dot products, 16 row groups per column.
+#include <atomic>
+
 #include "moe_internal.h"
 
 namespace moe {
@@ -190,7 +192,7 @@ __device__ __forceinline__ int lds_i16(uint32_t a) {
 // slow the arrivals' atomics.
 constexpr int kSyncCount = 0;
 constexpr int kSyncRelease = 32;
-constexpr int kSyncErr = 64;
+constexpr int kSyncErr = int(kSyncErrOffset / 4);
 constexpr uint32_t kSpinLimit = 1u << 20;
 
 // The release word as the launch found it. Every workgroup reads it before
@@ -1101,17 +1103,47 @@ __global__ __launch_bounds__(kF32Threads) void down_f32_kernel(
   }
 }
 
-int device_cus() {
-  static int cus = 0;
-  if (cus == 0) {
-    int dev = 0, n = 0;
-    if (hipGetDevice(&dev) == hipSuccess &&
-        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
-      cus = n;
-    else
-      cus = 256;
+// Per device: compute units and how many workgroups of each instantiation of
+// the persistent FFN kernel one CU holds, queried on the first launch on that
+// device and cached (several host threads may race to fill an entry; they
+// store the same values).
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_cus[kMaxDevices];
+std::atomic<int> g_resident[kMaxDevices][3];
+
+template <int MTX>
+constexpr int mtx_index() { return MTX == 1 ? 0 : MTX == 2 ? 1 : 2; }
+
+template <int MTX>
+int query_resident_per_cu() {
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, ffn_kernel<MTX>, kThreads, 0) != hipSuccess) return 0;
+  return n;
+}
+
+// Compute units of the current device and the workgroups of ffn_kernel<MTX>
+// that can be resident on the whole device at once (0 when unknown).
+template <int MTX>
+void device_limits(int &cus, int &resident) {
+  int dev = 0;
+  cus = 0;
+  resident = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return;
+  const bool cached = dev >= 0 && dev < kMaxDevices;
+  cus = cached ? g_cus[dev].load(std::memory_order_relaxed) : 0;
+  if (cus <= 0) {
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) {
+      cus = 0;
+      return;
+    }
+    if (cached) g_cus[dev].store(cus, std::memory_order_relaxed);
   }
-  return cus;
+  int per_cu = cached ? g_resident[dev][mtx_index<MTX>()].load(std::memory_order_relaxed) : 0;
+  if (per_cu <= 0) {
+    per_cu = query_resident_per_cu<MTX>();
+    if (cached && per_cu > 0) g_resident[dev][mtx_index<MTX>()].store(per_cu, std::memory_order_relaxed);
+  }
+  resident = per_cu * cus;
 }
 
 // Gate/up split for every possible active-expert count n (the count is only
@@ -1159,19 +1191,52 @@ void plan_gate_up(const Params &p, int G, UpPlan &up) {
   }
 }
 
+// One workgroup per CU at most (grid = min(items, CUs)), so that the whole
+// grid is resident together and its grid barriers cannot wait on a
+// workgroup that has not started. A device whose CUs cannot hold the grid
+// gets hipErrorCooperativeLaunchTooLarge instead of a launch.
 template <int MTX>
-void launch_ffn(int grid, const Params &p, const UpPlan &up, const moe_routing_t &r, hipStream_t s) {
+hipError_t ffn_grid(int items, int &grid) {
+  int cus = 0, resident = 0;
+  device_limits<MTX>(cus, resident);
+  if (cus <= 0) return hipErrorInvalidDevice;
+  grid = items < cus ? items : cus;
+  return resident < grid ? hipErrorCooperativeLaunchTooLarge : hipSuccess;
+}
+
+template <int MTX>
+hipError_t launch_ffn(int items, Params &p, const moe_routing_t &r, hipStream_t s) {
+  int grid = 0;
+  const hipError_t e = ffn_grid<MTX>(items, grid);
+  if (e != hipSuccess) return e;
+  UpPlan up;
+  plan_gate_up(p, grid, up);
   ffn_kernel<MTX><<<grid, kThreads, 0, s>>>(p, up, r.n_active, r.active_experts, r.expert_offsets);
+  return hipGetLastError();
+}
+
+int ffn_items(int B, int d, int E, int I, int k, const Workspace &plan) {
+  const int P = B * k;
+  const int max_active = E < P ? E : P;
+  return max_active * (ceil_div(I, kStripCols) * plan.up_slices + ceil_div(d, 2 * kStripCols));
 }
 
 }  // namespace
+
+hipError_t expert_ffn_launchable(moe_dtype_t dt, int B, int d, int E, int I, int k, const Workspace &plan) {
+  if (dt != MOE_BF16) return hipSuccess;
+  const int items = ffn_items(B, d, E, I, k, plan);
+  int grid = 0;
+  if (B <= 16) return ffn_grid<1>(items, grid);
+  if (B <= 32) return ffn_grid<2>(items, grid);
+  return ffn_grid<4>(items, grid);
+}
 
 hipError_t launch_expert_ffn(const void *x, const void *w_gate, const void *w_up,
                              const void *w_down, moe_dtype_t dt, int B, int d, int E, int I,
                              int k, const moe_routing_t &r, void *y, char *ws,
                              const Workspace &plan, hipStream_t s) {
   const int P = B * k;
-  const int max_active = E < P ? E : P;
   float *part = reinterpret_cast<float *>(ws + plan.down_part);
   int32_t *pos = reinterpret_cast<int32_t *>(ws + plan.pair_of_slot);
   if (dt == MOE_BF16) {
@@ -1199,21 +1264,12 @@ hipError_t launch_expert_ffn(const void *x, const void *w_gate, const void *w_up
     p.sync = reinterpret_cast<uint32_t *>(ws);
     p.grp_cnt = reinterpret_cast<uint32_t *>(ws + kGrpCntOffset);
     p.n_dstrips = ceil_div(d, 2 * kStripCols);
-    // One workgroup per CU at most, so that the whole grid is resident and
-    // the grid barriers cannot wait on a workgroup that has not started.
-    const int items = max_active * (ceil_div(I, kStripCols) * plan.up_slices + ceil_div(d, 2 * kStripCols));
-    const int cus = device_cus();
-    const int grid = items < cus ? items : cus;
-    UpPlan up;
-    plan_gate_up(p, grid, up);
+    const int items = ffn_items(B, d, E, I, k, plan);
     // An expert has at most B tokens: A tiles of 16 * MTX rows cover them
     // (experts with more than 64 tokens take several passes).
-    if (B <= 16)
-      launch_ffn<1>(grid, p, up, r, s);
-    else if (B <= 32)
-      launch_ffn<2>(grid, p, up, r, s);
-    else
-      launch_ffn<4>(grid, p, up, r, s);
+    if (B <= 16) return launch_ffn<1>(items, p, r, s);
+    if (B <= 32) return launch_ffn<2>(items, p, r, s);
+    return launch_ffn<4>(items, p, r, s);
   } else {
     float *h = reinterpret_cast<float *>(ws + plan.h);
     up_f32_kernel<<<dim3(ceil_div(I, kF32Cols), P), kF32Threads, 0, s>>>(

@@ -46,6 +46,8 @@ inline float lynx_bin_width(int E, int k) { return float(std::log(double(E) / do
 // use. Every call leaves the counters at zero; the barrier's release word
 // only grows. No other step writes them.
 constexpr size_t kSyncBytes = 2048;
+constexpr size_t kSyncErrOffset = 256;         // FFN: non-zero once a grid-barrier wait gave up
+static_assert(kSyncErrOffset + 4 <= MOE_WS_STATUS_BYTES, "status word inside the status bytes");
 constexpr size_t kRouteSelectCntOffset = 384;  // fused router + selection: tiles done
 constexpr size_t kRouterCntOffset = 512;
 constexpr int kTokGroup = 16;                      // tokens per combine group
@@ -117,6 +119,11 @@ hipError_t launch_route_select(const void *x, const void *w_g, const float *bias
 // workgroups; out[b] receives workgroup b's XOR of the words it read.
 constexpr int kReadStreamBlocks = 1024;
 hipError_t launch_read_stream(const void *src, size_t bytes, uint32_t *out, hipStream_t s);
+
+// Whether launch_expert_ffn can run these sizes on the current device (bf16:
+// its persistent grid fits the device's resident-workgroup limit). Launches
+// nothing; hipErrorCooperativeLaunchTooLarge when the grid cannot be resident.
+hipError_t expert_ffn_launchable(moe_dtype_t dt, int B, int d, int E, int I, int k, const Workspace &plan);
 
 hipError_t launch_expert_ffn(const void *x, const void *w_gate, const void *w_up,
                              const void *w_down, moe_dtype_t dt, int B, int d, int E, int I,

@@ -72,8 +72,11 @@
  *     captured into a HIP graph.
  *   - Every argument is checked on the host before any HIP call; a failed
  *     check returns an error code and enqueues nothing. No C++ exception
- *     crosses this interface. Calls hold no global state and are safe from
- *     several host threads on different streams with different workspaces.
+ *     crosses this interface. The only state kept between calls is, per
+ *     device, its compute-unit count and the expert FFN's resident-workgroup
+ *     limit, queried on the first call on that device and cached thread-
+ *     safely. Calls are safe from several host threads on different streams
+ *     with different workspaces.
  *   - Non-finite inputs give unspecified results.
  *
  * Supported envelope (else MOE_ERR_UNSUPPORTED): 1 <= B <= 256,
@@ -96,8 +99,16 @@ typedef enum {
   MOE_ERR_INVALID_ARG = 1, /* null/misaligned pointer, k > E, k0 or m out of range, ... */
   MOE_ERR_UNSUPPORTED = 2, /* sizes outside the supported envelope above              */
   MOE_ERR_WORKSPACE = 3,   /* workspace missing, misaligned or smaller than required  */
-  MOE_ERR_HIP = 4          /* a kernel launch failed (hipGetLastError)                 */
+  MOE_ERR_HIP = 4,         /* a kernel launch failed (hipGetLastError)                 */
+  MOE_ERR_RESIDENCY = 5,   /* the bf16 expert FFN's workgroups (one per compute unit)
+                              cannot all be resident on this device: nothing launched */
+  MOE_ERR_SYNC_TIMEOUT = 6 /* from moe_workspace_check: a grid-wide wait of the bf16
+                              expert FFN gave up in some call since the workspace was
+                              zero-filled; those calls' outputs are unspecified        */
 } moe_status_t;
+
+/* Bytes at the start of a workspace that moe_workspace_check reads. */
+#define MOE_WS_STATUS_BYTES 512
 
 typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype_t;
 
@@ -150,11 +161,24 @@ typedef struct {
  * every call leaves ready for the next one. The same workspace may serve
  * consecutive calls on one stream; calls that may overlap need separate
  * workspaces. The bf16 expert FFN runs one workgroup per compute unit and
- * needs all of them resident together: do not run it next to another kernel
- * that waits on work of its own. If a barrier wait nevertheless exceeds its
- * bound (about a million polls), the kernel sets the 32-bit word at byte 256
- * of the workspace to 1 and finishes with unspecified outputs. */
+ * needs all of them resident together: a device whose compute units cannot
+ * hold its grid gets MOE_ERR_RESIDENCY at launch; do not run it next to
+ * another kernel that waits on work of its own. If a grid-wide wait
+ * nevertheless exceeds its bound (about a million polls), the kernel records
+ * it in the workspace's status bytes, which stay set until the workspace is
+ * zero-filled again, and finishes with unspecified outputs (it never hangs);
+ * moe_workspace_check reports it. */
 size_t moe_workspace_bytes(int B, int d, int E, int I, int k, moe_dtype_t dt);
+
+/* Reads the status of a workspace: `status_host` is a HOST copy of the first
+ * MOE_WS_STATUS_BYTES bytes of the workspace (e.g. hipMemcpy after the
+ * stream has reached the calls to check), `bytes` its size. Returns
+ * MOE_ERR_SYNC_TIMEOUT if a grid-wide wait of the bf16 expert FFN gave up in
+ * any call since the workspace was last zero-filled, MOE_OK otherwise, and
+ * MOE_ERR_INVALID_ARG for a null pointer or bytes < MOE_WS_STATUS_BYTES.
+ * Host-only: makes no HIP call. Callers that cannot afford the copy after
+ * every call may check once after a batch of calls. */
+moe_status_t moe_workspace_check(const void *status_host, size_t bytes);
 
 /* Step 1 only: logits[B,E] (float32) = x W_g + bias. bias may be NULL (zero).
  * Uses the workspace (after the synchronisation words) for per-slice partial

@@ -36,10 +36,39 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_status_strings(lib):
-    for s in range(5):
-        assert L.status_string(s).startswith(
-            ["MOE_OK", "MOE_ERR_INVALID_ARG", "MOE_ERR_UNSUPPORTED", "MOE_ERR_WORKSPACE", "MOE_ERR_HIP"][s])
+    names = ["MOE_OK", "MOE_ERR_INVALID_ARG", "MOE_ERR_UNSUPPORTED", "MOE_ERR_WORKSPACE", "MOE_ERR_HIP",
+             "MOE_ERR_RESIDENCY", "MOE_ERR_SYNC_TIMEOUT"]
+    for s, name in enumerate(names):
+        assert L.status_string(s).startswith(name)
+        assert getattr(L, name) == s
     assert "unknown" in L.status_string(99)
+
+
+def test_header_status_codes_match_binding():
+    src = open(HEADER).read()
+    for name, val in re.findall(r"\b(MOE_ERR_[A-Z_]+|MOE_OK) = (\d+)", src):
+        assert getattr(L, name) == int(val), name
+    assert int(re.search(r"#define MOE_WS_STATUS_BYTES (\d+)", src).group(1)) == L.MOE_WS_STATUS_BYTES
+
+
+def test_workspace_check_reads_the_status_word(lib):
+    """A zero-filled workspace head is clean; the status word the expert FFN
+    sets when a grid-wide wait gives up (byte 256, written here from the
+    host) is reported as MOE_ERR_SYNC_TIMEOUT; other words (barrier count,
+    release word, counters) do not matter; short or null buffers are
+    rejected."""
+    head = bytearray(L.MOE_WS_STATUS_BYTES)
+    assert L.workspace_status(bytes(head)) == L.MOE_OK
+    head[0:4] = (7).to_bytes(4, "little")      # arrival count mid-launch
+    head[128:132] = (99).to_bytes(4, "little")  # release word (only grows)
+    head[384:388] = (3).to_bytes(4, "little")   # router + selection counter
+    assert L.workspace_status(bytes(head)) == L.MOE_OK
+    head[256:260] = (1).to_bytes(4, "little")
+    assert L.workspace_status(bytes(head)) == L.MOE_ERR_SYNC_TIMEOUT
+    head[256:260] = (0x100).to_bytes(4, "little")  # any bit of the word
+    assert L.workspace_status(bytes(head)) == L.MOE_ERR_SYNC_TIMEOUT
+    assert L.workspace_status(bytes(head[:L.MOE_WS_STATUS_BYTES - 1])) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_workspace_check(None, L.MOE_WS_STATUS_BYTES) == L.MOE_ERR_INVALID_ARG
 
 
 def test_workspace_bytes_envelope(lib):
