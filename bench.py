@@ -46,7 +46,8 @@ def _parse():
     ap.add_argument("--g", type=int, default=4, help="hier: tokens per request (--k0 is the request budget)")
     ap.add_argument("--rotate-bytes", type=float, default=2.0e9,
                     help="replicas are added until they hold this many distinct active bytes")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="oracle time with all threads (half of it again with 1 thread)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--sweep", default=None,
                     help="run every configured (config, B, policy) case; one JSON line each to this file")
@@ -175,27 +176,48 @@ def _traffic(workload):
     return int(t["fetch_bytes"] + t["write_bytes"])
 
 
-def _cpu_baseline(cfg, inp, B, policy, k0, m, active_bytes, seconds, g=0):
-    from threadpoolctl import threadpool_info
+def _cpu_threads():
+    """Host threads for the oracle: the CPUs this process may run on, capped
+    by OMP_NUM_THREADS when the environment sets it (a shared host's CPU
+    share)."""
+    n = len(os.sched_getaffinity(0))
+    env = os.environ.get("OMP_NUM_THREADS", "")
+    if env.isdigit() and int(env) > 0:
+        n = min(n, int(env))
+    return n
+
+
+def _time_oracle(args, kw, seconds, threads):
+    from threadpoolctl import threadpool_info, threadpool_limits
     from oracle import moe_oracle as orc
 
-    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    times = []
+    with threadpool_limits(limits=threads):
+        used = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        t_end = time.perf_counter() + seconds
+        while True:
+            t0 = time.perf_counter()
+            orc.moe_layer(*args, **kw)
+            times.append(time.perf_counter() - t0)
+            if (time.perf_counter() > t_end and len(times) >= 5) or len(times) >= 200:
+                break
+    return float(np.median(times)), len(times), int(used)
+
+
+def _cpu_baseline(cfg, inp, B, policy, k0, m, active_bytes, seconds, g=0):
     args = (inp["x"][:B], inp["w_g"], inp["bias"], inp["w_gate"], inp["w_up"], inp["w_down"],
             cfg.dtype, policy, cfg.k, k0, m)
     kw = {"g": g}
-    times = []
-    t_end = time.perf_counter() + seconds
-    while True:
-        t0 = time.perf_counter()
-        orc.moe_layer(*args, **kw)
-        times.append(time.perf_counter() - t0)
-        if time.perf_counter() > t_end or len(times) >= 200:
-            break
-    med = float(np.median(times))
-    return {"value": active_bytes / med / 1e9, "unit": "GB/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{len(times)} full oracle layer calls (numpy float64: router, selection, SwiGLU "
-                      f"over the active experts with bf16 widening) on the same B={B} batch; "
-                      f"median {med * 1e3:.1f} ms per call"}
+    affinity = len(os.sched_getaffinity(0))
+    med, n, used = _time_oracle(args, kw, seconds, _cpu_threads())
+    med1, n1, _ = _time_oracle(args, kw, seconds / 2, 1)
+    return {"value": active_bytes / med / 1e9, "unit": "GB/s", "cores": used, "kind": "oracle",
+            "cores_available": affinity,
+            "value_1_thread": active_bytes / med1 / 1e9,
+            "sample": f"{n} full oracle layer calls with {used} BLAS threads and {n1} with 1 thread "
+                      f"(numpy float64: router, selection, SwiGLU over the active experts with bf16 "
+                      f"widening) on the same B={B} batch; median {med * 1e3:.1f} ms per call "
+                      f"({med1 * 1e3:.1f} ms with 1 thread)"}
 
 
 def _policy_name(policy, k0, m, g):
@@ -214,6 +236,9 @@ def _run_case(cfg, B, policy, k0, m, inp, dev, args, with_cpu, g=0):
     # The expert FFN alone (one kernel for bf16): its average launch time.
     _, total_f = _time_steps(c.ffn, R, args.steps, args.warmup)
     ffn_ms = total_f / args.steps
+    # Every timed call shared this workspace: a grid-wide wait that gave up
+    # would have left its outputs unspecified.
+    c.L.check_workspace(c.ws)
     value = c.active_bytes / (ms_per_step * 1e-3) / 1e9
     ffn_gbps = c.active_bytes / (ffn_ms * 1e-3) / 1e9
     pol = _policy_name(policy, k0, m, g)
@@ -235,7 +260,9 @@ def _run_case(cfg, B, policy, k0, m, inp, dev, args, with_cpu, g=0):
         "config": {"workload": out_workload,
                    "batch": B, "policy": pol, "replicas": R},
         "layer_us": {"median": round(med * 1e3, 2), "p10": round(p10 * 1e3, 2),
-                     "p90": round(p90 * 1e3, 2), "mean": round(ms_per_step * 1e3, 2)},
+                     "p90": round(p90 * 1e3, 2), "mean": round(ms_per_step * 1e3, 2),
+                     "samples": len(per), "steps_per_sample": R,
+                     "note": "percentiles over graph replays, each the mean of its chained steps"},
         "n_active": c.n_active,
         "pairs": c.pairs,
         "active_expert_bytes": c.active_bytes,
@@ -319,7 +346,8 @@ def main():
                 inp = make_layer(cfg, max(cfg.batches))
                 dev = _upload(inp, cfg.dtype)
                 pols = [("topk", 0, 0, 0)] + [("oea", k0, 0, 0) for k0 in cfg.oea_k0] + \
-                       [("budget", 0, m, 0) for m in cfg.budget_m]
+                       [("budget", 0, m, 0) for m in cfg.budget_m] + \
+                       [("greedy", 0, m, 0) for m in cfg.budget_m]
                 if cname == "specdec_bf16":  # requests of 4 drafts
                     pols += [("hier", m // 4, m, 4) for m in cfg.budget_m]
                 if cname in ("qwen3_30b_bf16", "lynx_bf16"):
