@@ -21,7 +21,9 @@ MOE_ERR_WORKSPACE = 3
 MOE_ERR_HIP = 4
 MOE_ERR_RESIDENCY = 5
 MOE_ERR_SYNC_TIMEOUT = 6
+MOE_ERR_SCRATCH = 7
 MOE_WS_STATUS_BYTES = 512
+MOE_STATIC_SCRATCH_BYTES = 32 << 20
 
 MOE_F32 = 0
 MOE_BF16 = 1
@@ -34,7 +36,8 @@ MOE_POLICY_HIER = 4
 MOE_POLICY_LYNX = 5
 
 EXPORTS = ("moe_workspace_bytes", "moe_workspace_check", "moe_route", "moe_select",
-           "moe_expert_ffn", "moe_layer_decode", "moe_status_string", "moe_read_stream")
+           "moe_expert_ffn", "moe_layer_decode", "moe_layer_decode_static", "moe_status_string",
+           "moe_read_stream")
 
 
 class MoeError(RuntimeError):
@@ -81,6 +84,9 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.moe_layer_decode.restype = c_int
     lib.moe_layer_decode.argtypes = [vp, vp, vp, vp, vp, vp, c_int, c_int, c_int, c_int, c_int,
                                      Policy, vp, ctypes.POINTER(RoutingC), vp, vp, sz, vp]
+    lib.moe_layer_decode_static.restype = c_int
+    lib.moe_layer_decode_static.argtypes = [vp, vp, vp, vp, vp, vp, c_int, c_int, c_int, c_int, c_int,
+                                            Policy, vp, ctypes.POINTER(RoutingC), vp, vp]
     lib.moe_status_string.restype = ctypes.c_char_p
     lib.moe_status_string.argtypes = [c_int]
     lib.moe_workspace_check.restype = c_int
@@ -245,3 +251,20 @@ def moe_layer_decode(x, w_g, bias, w_gate, w_up, w_down, policy: Policy, logits,
                                    _ptr(w_down), _dt(x), B, d, E, I, policy, _ptr(logits),
                                    ctypes.byref(r), _ptr(y), _ptr(workspace), workspace.numel(),
                                    _stream(stream)))
+
+
+def moe_layer_decode_static(x, w_g, bias, w_gate, w_up, w_down, policy: Policy, logits,
+                            routing: Routing, y, stream=None):
+    """moe_layer_decode with the library's static device scratch instead of a
+    workspace (allocates nothing); calls on one device must not overlap."""
+    B, d = x.shape
+    E, d2, I = w_gate.shape
+    if d2 != d or tuple(w_g.shape) != (d, E) or tuple(w_up.shape) != (E, d, I) \
+            or tuple(w_down.shape) != (E, I, d) or tuple(y.shape) != (B, d):
+        raise ValueError("shape mismatch")
+    if tuple(logits.shape) != (B, E) or (routing.B, routing.E, routing.k) != (B, E, policy.k):
+        raise ValueError("logits/routing buffers do not match B, E, k")
+    r = routing.c_struct()
+    _check(load().moe_layer_decode_static(_ptr(x), _ptr(w_g), _ptr(bias), _ptr(w_gate), _ptr(w_up),
+                                          _ptr(w_down), _dt(x), B, d, E, I, policy, _ptr(logits),
+                                          ctypes.byref(r), _ptr(y), _stream(stream)))

@@ -14,7 +14,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmoe_decode.so")
-SOURCES = ["router.hip", "select.hip", "route_select.hip", "ffn.hip", "stream.hip", "api.cpp"]
+SOURCES = ["router.hip", "select.hip", "route_select.hip", "ffn.hip", "stream.hip", "static_scratch.hip",
+           "api.cpp"]
 ARCH = "gfx950"
 
 # Packed fp32 VALU forms are disabled for all device code.

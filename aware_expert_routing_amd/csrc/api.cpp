@@ -83,6 +83,45 @@ moe_status_t hip_status(hipError_t e) {
   return e == hipErrorCooperativeLaunchTooLarge ? MOE_ERR_RESIDENCY : MOE_ERR_HIP;
 }
 
+// Checks of every moe_layer_decode argument except the workspace.
+moe_status_t check_layer_args(const void *x, const void *w_g, const float *bias, const void *w_gate,
+                              const void *w_up, const void *w_down, moe_dtype_t dt, int B, int d,
+                              int E, int I, const moe_policy_t &policy, const float *logits,
+                              const moe_routing_t *routing, const void *y) {
+  if (!valid_dtype(dt)) return MOE_ERR_INVALID_ARG;
+  MOE_TRY(check_sizes(B, d, E, I, policy.k < 1 ? 1 : policy.k));
+  MOE_TRY(check_policy(policy, E));
+  MOE_TRY(check_dense(x));
+  MOE_TRY(check_dense(w_g));
+  MOE_TRY(check_dense(w_gate));
+  MOE_TRY(check_dense(w_up));
+  MOE_TRY(check_dense(w_down));
+  MOE_TRY(check_dense(y));
+  if (!logits || !aligned(logits, 4)) return MOE_ERR_INVALID_ARG;
+  if (bias && !aligned(bias, 4)) return MOE_ERR_INVALID_ARG;
+  return check_routing(routing, policy.kind == MOE_POLICY_BUDGET || policy.kind == MOE_POLICY_HIER);
+}
+
+// The layer's launches on stream s with workspace ws (planned by plan).
+moe_status_t layer_launches(const void *x, const void *w_g, const float *bias, const void *w_gate,
+                            const void *w_up, const void *w_down, moe_dtype_t dt, int B, int d,
+                            int E, int I, const moe_policy_t &policy, float *logits,
+                            const moe_routing_t *routing, void *y, char *ws, const Workspace &plan,
+                            hipStream_t s) {
+  if (dt == MOE_BF16) {
+    float *part = reinterpret_cast<float *>(ws + plan.router_part);
+    uint32_t *cnt = reinterpret_cast<uint32_t *>(ws + kRouteSelectCntOffset);
+    MOE_TRY(hip_status(launch_route_select(x, w_g, bias, B, d, E, logits, part, cnt, policy, *routing, s)));
+  } else {
+    float *part = reinterpret_cast<float *>(ws + plan.router_part);
+    uint32_t *cnt = reinterpret_cast<uint32_t *>(ws + kRouterCntOffset);
+    MOE_TRY(hip_status(launch_router(x, w_g, bias, dt, B, d, E, part, cnt, logits, s)));
+    MOE_TRY(hip_status(launch_select(logits, B, E, policy, *routing, s)));
+  }
+  return hip_status(launch_expert_ffn(x, w_gate, w_up, w_down, dt, B, d, E, I, policy.k, *routing,
+                                      y, ws, plan, s));
+}
+
 }  // namespace
 
 extern "C" {
@@ -144,35 +183,31 @@ moe_status_t moe_layer_decode(const void *x, const void *w_g, const float *bias,
                               moe_dtype_t dt, int B, int d, int E, int I, moe_policy_t policy,
                               float *logits, const moe_routing_t *routing, void *y,
                               void *workspace, size_t workspace_bytes, void *stream) {
-  if (!valid_dtype(dt)) return MOE_ERR_INVALID_ARG;
-  MOE_TRY(check_sizes(B, d, E, I, policy.k < 1 ? 1 : policy.k));
-  MOE_TRY(check_policy(policy, E));
-  MOE_TRY(check_dense(x));
-  MOE_TRY(check_dense(w_g));
-  MOE_TRY(check_dense(w_gate));
-  MOE_TRY(check_dense(w_up));
-  MOE_TRY(check_dense(w_down));
-  MOE_TRY(check_dense(y));
-  if (!logits || !aligned(logits, 4)) return MOE_ERR_INVALID_ARG;
-  if (bias && !aligned(bias, 4)) return MOE_ERR_INVALID_ARG;
-  MOE_TRY(check_routing(routing, policy.kind == MOE_POLICY_BUDGET || policy.kind == MOE_POLICY_HIER));
+  MOE_TRY(check_layer_args(x, w_g, bias, w_gate, w_up, w_down, dt, B, d, E, I, policy, logits, routing, y));
   const Workspace plan = plan_workspace(B, d, E, I, policy.k, dt);
   MOE_TRY(check_workspace(workspace, workspace_bytes, plan.total));
   MOE_TRY(hip_status(expert_ffn_launchable(dt, B, d, E, I, policy.k, plan)));
+  return layer_launches(x, w_g, bias, w_gate, w_up, w_down, dt, B, d, E, I, policy, logits, routing, y,
+                        static_cast<char *>(workspace), plan, static_cast<hipStream_t>(stream));
+}
+
+moe_status_t moe_layer_decode_static(const void *x, const void *w_g, const float *bias,
+                                     const void *w_gate, const void *w_up, const void *w_down,
+                                     moe_dtype_t dt, int B, int d, int E, int I, moe_policy_t policy,
+                                     float *logits, const moe_routing_t *routing, void *y,
+                                     void *stream) {
+  MOE_TRY(check_layer_args(x, w_g, bias, w_gate, w_up, w_down, dt, B, d, E, I, policy, logits, routing, y));
+  const Workspace plan = plan_workspace(B, d, E, I, policy.k, dt);
+  if (plan.total > kStaticScratchBytes) return MOE_ERR_SCRATCH;
+  MOE_TRY(hip_status(expert_ffn_launchable(dt, B, d, E, I, policy.k, plan)));
+  char *ws = nullptr;
+  MOE_TRY(hip_status(static_scratch_address(&ws)));
   hipStream_t s = static_cast<hipStream_t>(stream);
-  char *ws = static_cast<char *>(workspace);
-  if (dt == MOE_BF16) {
-    float *part = reinterpret_cast<float *>(ws + plan.router_part);
-    uint32_t *cnt = reinterpret_cast<uint32_t *>(ws + kRouteSelectCntOffset);
-    MOE_TRY(hip_status(launch_route_select(x, w_g, bias, B, d, E, logits, part, cnt, policy, *routing, s)));
-  } else {
-    float *part = reinterpret_cast<float *>(ws + plan.router_part);
-    uint32_t *cnt = reinterpret_cast<uint32_t *>(ws + kRouterCntOffset);
-    MOE_TRY(hip_status(launch_router(x, w_g, bias, dt, B, d, E, part, cnt, logits, s)));
-    MOE_TRY(hip_status(launch_select(logits, B, E, policy, *routing, s)));
-  }
-  return hip_status(launch_expert_ffn(x, w_gate, w_up, w_down, dt, B, d, E, I, policy.k, *routing,
-                                      y, ws, plan, s));
+  // The previous call's counters are back at zero unless it was cut short;
+  // zero them anyway, so that every call starts from a known state.
+  MOE_TRY(hip_status(clear_scratch_counters(ws, s)));
+  return layer_launches(x, w_g, bias, w_gate, w_up, w_down, dt, B, d, E, I, policy, logits, routing, y,
+                        ws, plan, s);
 }
 
 moe_status_t moe_workspace_check(const void *status_host, size_t bytes) {
@@ -202,6 +237,9 @@ const char *moe_status_string(moe_status_t status) {
       return "MOE_ERR_HIP: a kernel launch failed";
     case MOE_ERR_RESIDENCY:
       return "MOE_ERR_RESIDENCY: the expert FFN's workgroups cannot all be resident on this device";
+    case MOE_ERR_SCRATCH:
+      return "MOE_ERR_SCRATCH: the sizes need more scratch than the static array of "
+             "moe_layer_decode_static holds (MOE_STATIC_SCRATCH_BYTES)";
     case MOE_ERR_SYNC_TIMEOUT:
       return "MOE_ERR_SYNC_TIMEOUT: a grid-wide wait of the expert FFN gave up; outputs of the calls "
              "since the workspace was zero-filled are unspecified";

@@ -97,6 +97,10 @@ inline Workspace plan_workspace(int B, int d, int E, int I, int k, moe_dtype_t d
   return w;
 }
 
+// Size of the file-scope scratch array of moe_layer_decode_static (per
+// device); calls whose workspace plan exceeds it are refused.
+constexpr size_t kStaticScratchBytes = MOE_STATIC_SCRATCH_BYTES;
+
 // ------------------------------------------------------------- launchers
 // Each launcher enqueues on `s` and returns hipGetLastError().
 
@@ -129,5 +133,11 @@ hipError_t launch_expert_ffn(const void *x, const void *w_gate, const void *w_up
                              const void *w_down, moe_dtype_t dt, int B, int d, int E, int I,
                              int k, const moe_routing_t &r, void *y, char *ws,
                              const Workspace &plan, hipStream_t s);
+
+// moe_layer_decode_static's scratch: the current device's address of the
+// file-scope array (looked up once per device), and a launch that zeroes its
+// counter region on stream s.
+hipError_t static_scratch_address(char **out);
+hipError_t clear_scratch_counters(char *ptr, hipStream_t s);
 
 }  // namespace moe

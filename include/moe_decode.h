@@ -102,13 +102,18 @@ typedef enum {
   MOE_ERR_HIP = 4,         /* a kernel launch failed (hipGetLastError)                 */
   MOE_ERR_RESIDENCY = 5,   /* the bf16 expert FFN's workgroups (one per compute unit)
                               cannot all be resident on this device: nothing launched */
-  MOE_ERR_SYNC_TIMEOUT = 6 /* from moe_workspace_check: a grid-wide wait of the bf16
+  MOE_ERR_SYNC_TIMEOUT = 6, /* from moe_workspace_check: a grid-wide wait of the bf16
                               expert FFN gave up in some call since the workspace was
                               zero-filled; those calls' outputs are unspecified        */
+  MOE_ERR_SCRATCH = 7      /* moe_layer_decode_static: the sizes need more scratch than
+                              its static array holds (MOE_STATIC_SCRATCH_BYTES)        */
 } moe_status_t;
 
 /* Bytes at the start of a workspace that moe_workspace_check reads. */
 #define MOE_WS_STATUS_BYTES 512
+
+/* Size of the static scratch of moe_layer_decode_static, per device. */
+#define MOE_STATIC_SCRATCH_BYTES (32u << 20)
 
 typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype_t;
 
@@ -206,6 +211,29 @@ moe_status_t moe_layer_decode(const void *x, const void *w_g, const float *bias,
                               moe_dtype_t dt, int B, int d, int E, int I, moe_policy_t policy,
                               float *logits, const moe_routing_t *routing, void *y,
                               void *workspace, size_t workspace_bytes, void *stream);
+
+/* moe_layer_decode without a workspace, for callers that cannot allocate
+ * device memory (code under HIP graph capture, serving loops or harnesses
+ * that forbid allocation). Same arguments, outputs, checks and results as
+ * moe_layer_decode; the scratch memory is a static device array of
+ * MOE_STATIC_SCRATCH_BYTES that the library holds on every device it runs
+ * on until the process ends (looked up on the first call on a device).
+ *   - Sizes whose moe_workspace_bytes exceeds MOE_STATIC_SCRATCH_BYTES get
+ *     MOE_ERR_SCRATCH and enqueue nothing (at d = 2048, E = 128, I = 768,
+ *     k = 8 every B up to 64 fits).
+ *   - Every call on a device shares that device's array: calls that may
+ *     overlap in time on one device (different streams, no ordering between
+ *     them) race and give unspecified results. Calls ordered on one stream
+ *     are fine.
+ *   - Each call first zeroes the array's counters (one small kernel), so a
+ *     call cut short cannot affect the next one; a grid-wide wait that gives
+ *     up is not reported (moe_layer_decode with a workspace reports it).
+ *   - Allocates nothing: no hipMalloc, hipFree or allocating library call. */
+moe_status_t moe_layer_decode_static(const void *x, const void *w_g, const float *bias,
+                                     const void *w_gate, const void *w_up, const void *w_down,
+                                     moe_dtype_t dt, int B, int d, int E, int I, moe_policy_t policy,
+                                     float *logits, const moe_routing_t *routing, void *y,
+                                     void *stream);
 
 /* Static description of a status code. Never NULL. */
 const char *moe_status_string(moe_status_t status);

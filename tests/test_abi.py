@@ -37,7 +37,7 @@ def test_exports_every_declared_symbol(lib):
 
 def test_status_strings(lib):
     names = ["MOE_OK", "MOE_ERR_INVALID_ARG", "MOE_ERR_UNSUPPORTED", "MOE_ERR_WORKSPACE", "MOE_ERR_HIP",
-             "MOE_ERR_RESIDENCY", "MOE_ERR_SYNC_TIMEOUT"]
+             "MOE_ERR_RESIDENCY", "MOE_ERR_SYNC_TIMEOUT", "MOE_ERR_SCRATCH"]
     for s, name in enumerate(names):
         assert L.status_string(s).startswith(name)
         assert getattr(L, name) == s
@@ -49,6 +49,32 @@ def test_header_status_codes_match_binding():
     for name, val in re.findall(r"\b(MOE_ERR_[A-Z_]+|MOE_OK) = (\d+)", src):
         assert getattr(L, name) == int(val), name
     assert int(re.search(r"#define MOE_WS_STATUS_BYTES (\d+)", src).group(1)) == L.MOE_WS_STATUS_BYTES
+    m = re.search(r"#define MOE_STATIC_SCRATCH_BYTES \((\d+)u << (\d+)\)", src)
+    assert int(m.group(1)) << int(m.group(2)) == L.MOE_STATIC_SCRATCH_BYTES
+
+
+def _layer_static(lib, **kw):
+    a = dict(x=A, w_g=A, bias=None, wg=A, wu=A, wd=A, dt=L.MOE_BF16, B=16, d=2048, E=128, I=768,
+             pol=L.Policy(L.MOE_POLICY_TOPK, 8, 0, 0), logits=A, r=_routing(), y=A, s=None)
+    a.update(kw)
+    r = a["r"]
+    return lib.moe_layer_decode_static(a["x"], a["w_g"], a["bias"], a["wg"], a["wu"], a["wd"], a["dt"],
+                                       a["B"], a["d"], a["E"], a["I"], a["pol"], a["logits"],
+                                       ctypes.byref(r) if r is not None else None, a["y"], a["s"])
+
+
+def test_static_layer_refuses_sizes_beyond_its_scratch(lib):
+    """moe_layer_decode_static refuses, before any HIP call, sizes whose
+    workspace would not fit its static scratch (the Qwen3-235B-shaped layer
+    at B = 64 needs about 59 MB), and checks its arguments like
+    moe_layer_decode."""
+    assert lib.moe_workspace_bytes(64, 4096, 128, 1536, 8, L.MOE_BF16) > L.MOE_STATIC_SCRATCH_BYTES
+    assert _layer_static(lib, B=64, d=4096, I=1536) == L.MOE_ERR_SCRATCH
+    assert lib.moe_workspace_bytes(64, 2048, 128, 768, 8, L.MOE_BF16) <= L.MOE_STATIC_SCRATCH_BYTES
+    assert _layer_static(lib, x=None) == L.MOE_ERR_INVALID_ARG
+    assert _layer_static(lib, r=None) == L.MOE_ERR_INVALID_ARG
+    assert _layer_static(lib, B=300) == L.MOE_ERR_UNSUPPORTED
+    assert _layer_static(lib, pol=L.Policy(L.MOE_POLICY_OEA, 8, 0, 0)) == L.MOE_ERR_INVALID_ARG
 
 
 def test_workspace_check_reads_the_status_word(lib):
