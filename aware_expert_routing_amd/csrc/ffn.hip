@@ -117,6 +117,9 @@ constexpr int kPolicyDevice = 16;
 // with it, which was measured to shorten every stage of the kernel (the
 // weights then do not displace reused lines in the caches).
 constexpr int kPolicyStream = 2;
+// SC0 alone: the load skips the compute unit's L1 and reads the XCD's L2,
+// which holds the latest data stored from this XCD.
+constexpr int kPolicyL2 = 1;
 
 // Copies 16 bytes per lane from buffer offset voff + soff into LDS at
 // dst + 16*lane. Offsets at or past the end of the buffer read as zero.
@@ -673,17 +676,35 @@ __device__ __forceinline__ void barrier_no_wait() {
   asm volatile("" ::: "memory");
 }
 
-// Counter of (token group grp, down strip) on a 128-byte line of its own.
-__device__ __forceinline__ uint32_t *group_counter(const Params &p, int grp, int strip) {
-  return p.grp_cnt + (size_t(strip) * kTokGroups + grp) * kCntStride;
+// Counter of (token group grp, down strip) on a 128-byte line of its own: a
+// 64-bit word holding, over the passes counted so far, S0 = sum of run
+// (bits 0-15: filled slots counted), S1 = sum of run * x (bits 16-31) and
+// S2 = sum of run * x^2 (bits 32-63), x being the XCD each pass ran on. By
+// Cauchy-Schwarz, S1^2 == S0 * S2 exactly when every pass ran on one XCD,
+// which is then x = S1 / S0.
+__device__ __forceinline__ uint64_t *group_counter(const Params &p, int grp, int strip) {
+  return reinterpret_cast<uint64_t *>(p.grp_cnt + (size_t(strip) * kTokGroups + grp) * kCntStride);
 }
+
+// The XCD (accelerator complex die) this wave runs on: bits 3:0 of the
+// XCC_ID hardware register.
+__device__ __forceinline__ uint32_t xcd_id() { return __builtin_amdgcn_s_getreg((3 << 11) | 20) & 15u; }
 
 // y over 128-column strip `strip` for the tokens of group grp: thread i takes
 // token 16*grp + i/16 and columns 8*(i%16) .. +7 of the strip, adding
 // w[t,j] * part[t*k+j] in slot order (empty slots skipped). Slots are taken
 // eight at a time with every load of a round issued before the first use.
+// The rows were stored with device-scope stores, which also update the L2 of
+// the storing XCD; when every row of the group's strip came from this
+// workgroup's XCD (`local`), they are read through that L2, else from the
+// device-coherent level.
 static_assert(kThreads == kTokGroup * (2 * kStripCols / 8), "one thread per token and 8 columns");
-__device__ __forceinline__ void combine_group(const Params &p, int grp, int strip) {
+__device__ __forceinline__ float4 ld_part4(__amdgpu_buffer_rsrc_t r, uint32_t off, bool local) {
+  const f32x4_t v = local ? __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, int(off), 0, kPolicyL2))
+                          : __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, int(off), 0, kPolicyDevice));
+  return make_float4(v[0], v[1], v[2], v[3]);
+}
+__device__ __forceinline__ void combine_group(const Params &p, int grp, int strip, bool local) {
   const int t = grp * kTokGroup + (threadIdx.x >> 4);
   const int col = strip * 2 * kStripCols + (threadIdx.x & 15) * 8;
   if (t >= p.B || col >= p.d) return;
@@ -701,8 +722,8 @@ __device__ __forceinline__ void combine_group(const Params &p, int grp, int stri
         id[jj] = p.ids[slot];
         w[jj] = p.w[slot];
         const uint32_t off = (uint32_t(slot) * uint32_t(p.d) + uint32_t(col)) * 4u;
-        v[jj][0] = ld_dev4(rp, off);
-        v[jj][1] = ld_dev4(rp, off + 16u);
+        v[jj][0] = ld_part4(rp, off, local);
+        v[jj][1] = ld_part4(rp, off + 16u, local);
       }
     }
 #pragma unroll
@@ -752,24 +773,29 @@ __device__ __forceinline__ void finish_down(const Cursor &c, const Params &p, un
     const bool first = lane < T && (lane == 0 || prev != grp);
     const unsigned long long fb = __ballot(first);
     bool mine = false;
+    int local = 0;
     if (first) {
       const unsigned long long above = lane == 63 ? 0ull : (fb >> (lane + 1));
-      const int run = above ? __builtin_ctzll(above) + 1 : T - lane;
-      const uint32_t before = __hip_atomic_fetch_add(group_counter(p, grp, c.strip), uint32_t(run),
-                                                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      mine = before + uint32_t(run) == gfill[grp];
+      const uint64_t run = above ? __builtin_ctzll(above) + 1 : T - lane;
+      const uint64_t x = xcd_id();
+      const uint64_t add = run | ((run * x) << 16) | ((run * x * x) << 32);
+      const uint64_t now = __hip_atomic_fetch_add(group_counter(p, grp, c.strip), add,
+                                                  __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + add;
+      const uint64_t s0 = now & 0xFFFFu, s1 = (now >> 16) & 0xFFFFu, s2 = now >> 32;
+      mine = s0 == gfill[grp];
+      local = mine && s1 * s1 == s0 * s2 && s1 == s0 * x;
     }
     const unsigned long long b = __ballot(mine);
-    if (mine) last[__builtin_amdgcn_mbcnt_hi(uint32_t(b >> 32), __builtin_amdgcn_mbcnt_lo(uint32_t(b), 0))] = grp;
+    if (mine) last[__builtin_amdgcn_mbcnt_hi(uint32_t(b >> 32), __builtin_amdgcn_mbcnt_lo(uint32_t(b), 0))] = grp | (local << 16);
     if (lane == 0) *n_last = __popcll(b);
   }
   __syncthreads();
   const int n = *n_last;
   for (int q = 0; q < n; ++q) {
-    const int grp = last[q];
-    combine_group(p, grp, c.strip);
+    const int grp = last[q] & 0xFFFF;
+    combine_group(p, grp, c.strip, (last[q] >> 16) != 0);
     if (threadIdx.x == 0)
-      __hip_atomic_store(group_counter(p, grp, c.strip), 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(group_counter(p, grp, c.strip), uint64_t(0), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   __syncthreads();
 }
