@@ -224,7 +224,7 @@ def moe_read_stream(src, out, stream=None):
                                   _stream(stream)))
 
 
-def moe_expert_ffn(x, w_gate, w_up, w_down, routing: Routing, y, workspace, stream=None):
+def moe_expert_ffn(x, w_gate, w_up, w_down, routing: Routing, y, workspace, stream=None, lib=None):
     B, d = x.shape
     E, d2, I = w_gate.shape
     if d2 != d or tuple(w_up.shape) != (E, d, I) or tuple(w_down.shape) != (E, I, d):
@@ -232,7 +232,7 @@ def moe_expert_ffn(x, w_gate, w_up, w_down, routing: Routing, y, workspace, stre
     if tuple(y.shape) != (B, d) or y.dtype != x.dtype:
         raise ValueError("y must be [B,d] in the input dtype")
     r = routing.c_struct()
-    _check(load().moe_expert_ffn(_ptr(x), _ptr(w_gate), _ptr(w_up), _ptr(w_down), _dt(x), B, d, E,
+    _check((lib or load()).moe_expert_ffn(_ptr(x), _ptr(w_gate), _ptr(w_up), _ptr(w_down), _dt(x), B, d, E,
                                  I, routing.k, ctypes.byref(r), _ptr(y), _ptr(workspace),
                                  workspace.numel(), _stream(stream)))
 

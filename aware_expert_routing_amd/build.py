@@ -30,30 +30,48 @@ def _hipcc() -> str:
     raise RuntimeError("hipcc not found")
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
+# Measurement library: the same sources with the expert FFN's phase stamps
+# compiled in (MOE_PHASE_STAMPS); bench.py --phase-timeline loads it. The
+# product library never contains them.
+PHASES_LIB = os.path.join(PKG, "libmoe_decode_phases.so")
+PHASES_DEFINE = "-DMOE_PHASE_STAMPS"
+
+
+def _compile(src: str, defines=()) -> str:
+    tag = "_phases" if defines else ""
+    obj = os.path.join(BUILD, os.path.splitext(src)[0] + tag + ".o")
     path = os.path.join(CSRC, src)
     lang = ["-x", "hip"] if src.endswith(".hip") else []
-    cmd = [_hipcc(), *COMMON, *DEVICE_FLAGS, *lang, "-c", path, "-o", obj]
+    cmd = [_hipcc(), *COMMON, *DEVICE_FLAGS, *defines, *lang, "-c", path, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every HIP/C++ source and link the shared library. Returns its path."""
-    os.makedirs(BUILD, exist_ok=True)
-    with ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
+def _link(objs, out: str) -> None:
+    tmp = out + ".tmp"
     cmd = [_hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every HIP/C++ source and link the shared library, and the
+    measurement library (the expert FFN with phase stamps). Returns the
+    product library's path."""
+    os.makedirs(BUILD, exist_ok=True)
+    jobs = [(src, ()) for src in SOURCES] + [("ffn.hip", (PHASES_DEFINE,))]
+    with ThreadPoolExecutor(max_workers=min(8, len(jobs))) as ex:
+        objs = list(ex.map(lambda j: _compile(*j), jobs))
+    product = objs[:len(SOURCES)]
+    _link(product, LIB)
+    phases = [o for o, src in zip(product, SOURCES) if src != "ffn.hip"] + [objs[-1]]
+    _link(phases, PHASES_LIB)
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} and {PHASES_LIB}")
     return LIB
 
 

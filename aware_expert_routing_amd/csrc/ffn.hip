@@ -33,6 +33,34 @@
 
 #include "moe_internal.h"
 
+// Measurement build only (compiled with -DMOE_PHASE_STAMPS into a separate
+// library; the product build compiles all of this away): lane 0 of every
+// workgroup records the 100 MHz s_memrealtime counter at the phase
+// boundaries into stamps[workgroup][64]: 0 start, 1 routing lists in LDS,
+// 2 first stage computed, 3 gate/up done, 4 past the first grid barrier,
+// 5 first down stages landed, 6 a down item's last stage computed, 7 its
+// rows stored, 8 counted, 9 a combine done, 10 end; 16 + s: stage s passed
+// its wait (bit 63 set for a down stage), s < 48.
+#ifdef MOE_PHASE_STAMPS
+#define MOE_STAMP(i)                                                                    \
+  do {                                                                                  \
+    if (threadIdx.x == 0 && p.stamps) p.stamps[blockIdx.x * 64 + (i)] = __builtin_amdgcn_s_memrealtime(); \
+  } while (0)
+#define MOE_STAGE_STAMP(s, down)                                                          \
+  do {                                                                                    \
+    if (threadIdx.x == 0 && p.stamps && (s) < 48)                                         \
+      p.stamps[blockIdx.x * 64 + 16 + (s)] =                                              \
+          __builtin_amdgcn_s_memrealtime() | ((down) ? (1ull << 63) : 0ull);              \
+  } while (0)
+#else
+#define MOE_STAMP(i) \
+  do {           \
+  } while (0)
+#define MOE_STAGE_STAMP(s, down) \
+  do {                       \
+  } while (0)
+#endif
+
 namespace moe {
 namespace {
 
@@ -49,7 +77,6 @@ constexpr int kRowBytes = kStripCols * 2;       // one strip row of bf16
 constexpr int kWTile = kBK * kRowBytes;         // bytes of one weight matrix per stage
 constexpr int kMaxTok = 64;                     // tokens per pass (4 MFMA row tiles)
 constexpr int kMaxPairs = kMaxB * kMaxK;
-constexpr int kSliceCost = 8;  // stages' worth of time the sliced gate/up path adds (measured)
 constexpr int kRsrcWord3 = 0x00020000;          // raw buffer, gfx9 data format
 constexpr int kLdsBytes = 160 * 1024;
 static_assert(kStripCols == 64 && kBK == 128, "tile constants");
@@ -243,6 +270,33 @@ __device__ __forceinline__ void grid_barrier_wave(uint32_t *sync, uint32_t base,
   }
 }
 
+// Stages per gate/up item for `tiles` gate/up tiles (active expert, 64-column
+// strip of I) of nblk stages each on G workgroups: nblk (whole-d tiles, h
+// formed in the epilogue) or the stages of one of 2 up to `planned` d slices
+// (the partial sums the workspace holds). The cost of a split is its busiest
+// workgroup's items times (stages per item + kFinishStages): after each
+// sliced item a workgroup waits for its partial sums to be stored and
+// counted, and the workgroup completing a tile forms its h, a few round trips
+// to memory under full load (about four stages' time, measured). The
+// cheapest wins, ties to whole tiles and then to fewer slices (fewer partial
+// sums to store and add). More tiles than tile counters take whole d.
+constexpr int kFinishStages = 4;
+__host__ __device__ inline int split_stages(int tiles, int nblk, int planned, int G) {
+  int best = nblk;
+  int best_cost = (tiles + G - 1) / G * nblk;
+  if (tiles > kMaxTileCounters) return best;
+  for (int sl = 2; sl <= planned; ++sl) {
+    const int b = (nblk + sl - 1) / sl;
+    const int items = tiles * ((nblk + b - 1) / b);
+    const int cost = (items + G - 1) / G * (b + kFinishStages);
+    if (cost < best_cost) {
+      best_cost = cost;
+      best = b;
+    }
+  }
+  return best;
+}
+
 struct Params {
   const uint16_t *x;          // [B, d]
   const uint16_t *W[3];       // G, U: [E, d, I]; D: [E, I, d]
@@ -258,7 +312,11 @@ struct Params {
   const int32_t *pair_token;  // [P]
   const int32_t *pair_slot;   // [P]
   uint32_t *sync;             // grid-barrier words
+#ifdef MOE_PHASE_STAMPS
+  uint64_t *stamps;           // measurement build: phase stamps
+#endif
   uint32_t *grp_cnt;          // per (strip, token group): slots counted, one 128-byte line each
+  uint32_t *tile_cnt;         // per gate/up tile (sliced path): d slices counted
   int n_dstrips;              // 128-column strips of d
 };
 
@@ -632,17 +690,33 @@ __device__ __forceinline__ void epilogue(const Cursor &c, const Params &p, uint3
     }
 }
 
-// h = SiLU(g) * u from the slice partial sums, spread over waves 0 and 1 of
-// every workgroup (threads 0..127). All loads of a lane are issued before the
-// first is used; the stores have completed when it returns.
-__device__ __forceinline__ void h_phase_waves01(const Params &p, int total) {
-  const int q4 = p.I / 4;
-  const int n = total * q4;
+// End of a gate/up item of the sliced path (every pass of it has stored its
+// partial sums of g and u, device scope). The item counts itself on its
+// tile's counter; the workgroup that brings the count to the number of d
+// slices forms h = SiLU(g) * u for the tile's 64 columns and every token of
+// the expert from the slices' partial sums, added in slice order, and puts
+// the counter back to zero. So h is complete once every workgroup has
+// finished its gate/up items, and one grid barrier separates gate/up from
+// down. `flag` is an int in LDS.
+__device__ __forceinline__ void finish_up(const Cursor &c, const Params &p, int *flag) {
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t *cnt = p.tile_cnt + size_t(c.item / p.slices) * kTileCntStride;
+    const uint32_t before = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const bool last = before + 1 == uint32_t(p.slices);
+    if (last) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    *flag = last;
+  }
+  __syncthreads();
+  if (!*flag) return;
   const uint32_t blk = uint32_t(p.P) * uint32_t(p.I) * 4u;  // bytes of one [P][I] block
-  for (int idx = blockIdx.x * 128 + threadIdx.x; idx < n; idx += gridDim.x * 128) {
-    const int pr = idx / q4;
-    const int c = (idx - pr * q4) * 4;
-    const uint32_t off = (uint32_t(pr) * uint32_t(p.I) + uint32_t(c)) * 4u;
+  const int col0 = c.strip * kStripCols;
+  for (int u = threadIdx.x; u < c.T * (kStripCols / 4); u += kThreads) {
+    const int m = u / (kStripCols / 4);
+    const int col = col0 + (u - m * (kStripCols / 4)) * 4;  // I % 8 == 0: col < I means col + 3 < I
+    if (col >= p.I) continue;
+    const uint32_t off = (uint32_t(c.p0 + m) * uint32_t(p.I) + uint32_t(col)) * 4u;
     float4 gv[kUpMaxSlices], uv[kUpMaxSlices];
 #pragma unroll
     for (int s = 0; s < kUpMaxSlices; ++s) {
@@ -651,21 +725,20 @@ __device__ __forceinline__ void h_phase_waves01(const Params &p, int total) {
         uv[s] = ld_dev4(make_rsrc(p.gpart + size_t(s * 2 + 1) * p.P * p.I, blk), off);
       }
     }
-    float4 g = make_float4(0, 0, 0, 0), u = make_float4(0, 0, 0, 0);
+    float4 g = make_float4(0, 0, 0, 0), v = make_float4(0, 0, 0, 0);
 #pragma unroll
     for (int s = 0; s < kUpMaxSlices; ++s) {
       if (s < p.slices) {
         g.x += gv[s].x; g.y += gv[s].y; g.z += gv[s].z; g.w += gv[s].w;
-        u.x += uv[s].x; u.y += uv[s].y; u.z += uv[s].z; u.w += uv[s].w;
+        v.x += uv[s].x; v.y += uv[s].y; v.z += uv[s].z; v.w += uv[s].w;
       }
     }
-    const uint64_t o = uint64_t(f32_to_bf16(silu(g.x) * u.x)) |
-                       (uint64_t(f32_to_bf16(silu(g.y) * u.y)) << 16) |
-                       (uint64_t(f32_to_bf16(silu(g.z) * u.z)) << 32) |
-                       (uint64_t(f32_to_bf16(silu(g.w) * u.w)) << 48);
-    st_dev(reinterpret_cast<uint64_t *>(p.h + size_t(pr) * p.I + c), o);
+    const uint64_t o = uint64_t(f32_to_bf16(silu(g.x) * v.x)) |
+                       (uint64_t(f32_to_bf16(silu(g.y) * v.y)) << 16) |
+                       (uint64_t(f32_to_bf16(silu(g.z) * v.z)) << 32) |
+                       (uint64_t(f32_to_bf16(silu(g.w) * v.w)) << 48);
+    st_dev(reinterpret_cast<uint64_t *>(p.h + size_t(c.p0 + m) * p.I + col), o);
   }
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
 // s_barrier without the wait for outstanding memory operations that
@@ -763,8 +836,10 @@ __device__ __forceinline__ void finish_down(const Cursor &c, const Params &p, un
   int32_t *last = reinterpret_cast<int32_t *>(meta + kMetaLast);
   int32_t *n_last = reinterpret_cast<int32_t *>(meta + kMetaNLast);
   const uint32_t *gfill = reinterpret_cast<const uint32_t *>(meta + kMetaGFill);
+  MOE_STAMP(6);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
+  MOE_STAMP(7);
   if (wave == 0) {
     // The first lane of each run of lanes in one group adds the run's
     // length (an expert's tokens ascend, so a group is one run).
@@ -790,6 +865,7 @@ __device__ __forceinline__ void finish_down(const Cursor &c, const Params &p, un
     if (lane == 0) *n_last = __popcll(b);
   }
   __syncthreads();
+  MOE_STAMP(8);
   const int n = *n_last;
   for (int q = 0; q < n; ++q) {
     const int grp = last[q] & 0xFFFF;
@@ -798,6 +874,7 @@ __device__ __forceinline__ void finish_down(const Cursor &c, const Params &p, un
       __hip_atomic_store(group_counter(p, grp, c.strip), uint64_t(0), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   __syncthreads();
+  if (n) MOE_STAMP(9);
 }
 
 // y over the strips of token groups that have no filled slot at all (no
@@ -817,26 +894,25 @@ __device__ __forceinline__ void zero_empty_groups(const Params &p, const unsigne
 
 // The change from gate/up to down in a workgroup: every gate/up stage of it
 // has been consumed and no down stage issued (the producer stops at the first
-// one); `first` is the next stage index. Wave 0 meets the grid at the first
-// barrier (gate/up partial sums complete); waves 0 and 1 then form this
-// workgroup's share of h, and wave 0 meets the grid again (h complete).
-// Meanwhile waves 2 and 3 copy the weights of the next kD down stages, all
-// four shares, so those copies overlap the barriers without delaying the
-// waits of waves 0 and 1 (vmcnt completes in order). Then every wave copies
-// its h rows of those stages and waits for all of them.
+// one); `first` is the next stage index. Wave 0 meets the grid at the
+// barrier (h complete). Meanwhile waves 2 and 3 copy the weights of the next
+// kD down stages, all four shares, so those copies overlap the barrier
+// without delaying the wait of wave 0 (vmcnt completes in order). Then every
+// wave copies its h rows of those stages and waits for all of them.
 template <int MTX>
 __device__ __forceinline__ void change_to_down(const Params &p, const Stream<MTX> &st, Cursor &prod,
                                                int &issued, int first, unsigned char *stages,
-                                               int total, uint32_t rel_base) {
+                                               uint32_t rel_base) {
   using S = Shape<2, MTX>;
   constexpr int kS = S::kStages;
   constexpr int kD = kS - 1;
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's gate/up stores
+  MOE_STAMP(3);
   __syncthreads();
-  const bool sliced = p.slices > 1;  // else the gate/up epilogues formed h
+  // h is complete once every workgroup is here (the gate/up epilogues, or
+  // the last slice of each tile, formed it).
   if (st.wave == 0) {
-    if (sliced) grid_barrier_wave(p.sync, rel_base, 1, false);
-    else grid_barrier_wave(p.sync, rel_base, 1, true);
+    grid_barrier_wave(p.sync, rel_base, 1, true);
   } else if (st.wave >= 2) {
     Cursor q = prod;
     for (int n = 0; n < kD && q.valid; ++n) {
@@ -847,30 +923,27 @@ __device__ __forceinline__ void change_to_down(const Params &p, const Stream<MTX
     }
   }
   barrier_no_wait();
-  if (sliced) {
-    if (st.wave < 2) h_phase_waves01(p, total);
-    barrier_no_wait();
-    if (st.wave == 0) grid_barrier_wave(p.sync, rel_base, 2, true);
-    barrier_no_wait();
-  }
+  MOE_STAMP(4);
   for (int n = 0; n < kD && prod.valid; ++n) {
     st.issue_a(prod, stages + ((first + n) % kS) * S::kSlot);
     st.advance(prod);
     ++issued;
   }
   wait_barrier<0>();
+  MOE_STAMP(5);
 }
 
 // The whole bf16 expert FFN in one persistent kernel (one workgroup per CU,
 // all resident together):
 //   1. gate/up items stream G and U and store slice partial sums;
-//   2. grid barrier; h = SiLU(g) * u over the grid; grid barrier
-//      (change_to_down);
+//   2. h = SiLU(g) * u, formed by the epilogue of a whole-d tile or by the
+//      workgroup that completes a tile's last d slice (finish_up); one
+//      grid barrier (change_to_down);
 //   3. down items stream D with h as the A operand and store rows by token
 //      slot; each token's strip of y is formed by the workgroup that
 //      completes it (finish_down).
 // The first down stages' weights are in flight while the workgroup waits at
-// the grid barriers; their A tiles are copied once h is complete.
+// the grid barrier; their A tiles are copied once h is complete.
 template <int MTX>
 __global__ __launch_bounds__(kThreads, 1) void ffn_kernel(Params p, const UpPlan up,
                                                           const int32_t *__restrict__ n_active,
@@ -879,6 +952,7 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_kernel(Params p, const UpPlan
   using S = Shape<2, MTX>;
   constexpr int kS = S::kStages;
   constexpr int kD = kS - 1;  // stages in flight ahead of the one in use
+  MOE_STAMP(0);
   __shared__ __attribute__((aligned(1024))) unsigned char lds[kS * S::kSlot + kMetaBytes];
   unsigned char *stages = lds;
   unsigned char *meta = lds + kS * S::kSlot;
@@ -940,6 +1014,7 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_kernel(Params p, const UpPlan
   }
   __syncthreads();
   zero_empty_groups(p, meta);
+  MOE_STAMP(1);
 
   // The gate/up split for this many active experts, chosen on the host
   // (plan_gate_up): stages of kBK rows per d slice, all of d for whole tiles.
@@ -948,21 +1023,20 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_kernel(Params p, const UpPlan
     p.slices = int(e >> 8);
     p.slice_rows = p.slices == 1 ? p.d : int(e & 0xFFu) * kBK;
   } else {
-    // 64-token passes: the same rule with the planned slices, decided here
-    // (reading the table slowed this instantiation's stage loop by 4-6%).
-    const int G = int(gridDim.x);
+    // 64-token passes: decided here, by a simpler rule (reading the table,
+    // or running split_stages here, slowed this instantiation's stage loop
+    // by 2-6%): as many of the planned slices as leave every item a
+    // workgroup of its own, else whole d.
     const int up_tiles = nact * ((p.I + kStripCols - 1) / kStripCols);
-    bool whole;
-    if (up_tiles <= G) {
-      whole = 5 * up_tiles >= 3 * G;
-    } else {
-      const int whole_span = ((up_tiles + G - 1) / G) * ((p.d + kBK - 1) / kBK);
-      const int sliced_span = ((up_tiles * p.slices + G - 1) / G) * (p.slice_rows / kBK) + kSliceCost;
-      whole = p.slices == 1 || whole_span <= sliced_span;
-    }
-    if (whole) {
+    const int nblk = (p.d + kBK - 1) / kBK;
+    const int sl = min(p.slices, int(gridDim.x) / max(up_tiles, 1));
+    if (sl <= 1 || up_tiles > kMaxTileCounters) {
       p.slices = 1;
       p.slice_rows = p.d;
+    } else {
+      const int blk = (nblk + sl - 1) / sl;
+      p.slices = (nblk + blk - 1) / blk;
+      p.slice_rows = blk * kBK;
     }
   }
 
@@ -992,7 +1066,7 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_kernel(Params p, const UpPlan
   bool h_ready = false;
   for (int s = 0; cons.valid; ++s) {
     if (!cons.up && !h_ready) {
-      change_to_down<MTX>(p, st, prod, issued, s, stages, total, rel_base);
+      change_to_down<MTX>(p, st, prod, issued, s, stages, rel_base);
       h_ready = true;
     }
     // Stage s must have landed; the stages issued after it may stay in flight
@@ -1006,12 +1080,14 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_kernel(Params p, const UpPlan
     }
     // Every wave is past stage s-1, so its slot takes stage s+kD, whose
     // copies are issued in two halves during the compute of stage s.
+    MOE_STAGE_STAMP(s, !cons.up);
     const bool fill = prod.valid && (prod.up || h_ready);
     unsigned char *fslot = stages + ((s + kD) % kS) * S::kSlot;
     compute_stage<MTX>(base + uint32_t((s % kS) * S::kSlot), st.trc, st.xrd, st.tp(cons), acc,
                        [&](int half) {
                          if (fill) st.issue_half(prod, fslot, half);
                        });
+    if (s == 0) MOE_STAMP(2);
     if (fill) {
       ++issued;
       st.advance(prod);
@@ -1020,10 +1096,13 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_kernel(Params p, const UpPlan
       epilogue<MTX>(cons, p, st.meta, st.wave, st.lane, acc);
       clear(acc);
       if (!cons.up) finish_down(cons, p, meta, st.wave, st.lane);
+      else if (p.slices > 1 && (cons.pass + 1) * kMaxTok >= cons.T)
+        finish_up(cons, p, reinterpret_cast<int *>(meta + kMetaNLast));
     }
     st.advance(cons);
   }
-  if (!h_ready) change_to_down<MTX>(p, st, prod, issued, 0, stages, total, rel_base);  // no down items here
+  if (!h_ready) change_to_down<MTX>(p, st, prod, issued, 0, stages, rel_base);  // no down items here
+  MOE_STAMP(10);
 }
 
 // ------------------------------------------------------------- combine (f32)
@@ -1172,21 +1251,8 @@ void device_limits(int &cus, int &resident) {
   resident = per_cu * cus;
 }
 
-// Gate/up split for every possible active-expert count n (the count is only
-// known on the device). A gate/up tile is (active expert, 64-column strip of
-// I). Whole-d tiles when the tiles fill enough of the grid to keep HBM busy:
-// each tile then forms its h columns itself and the grid meets once.
-// Otherwise slices of d spread the gate/up work over the grid and h is
-// formed from their partial sums between two grid barriers. With more tiles
-// than workgroups, the path whose busiest workgroup streams fewer stages
-// wins, the sliced one paying kSliceCost stages for its h phase and second
-// barrier (a few tiles past the grid would otherwise double the phase). A
-// sliced split takes the slice count, 2 up to the planned one (whose partial
-// sums the workspace holds), whose busiest workgroup streams the fewest
-// stages, ties to fewer slices (fewer, longer items and fewer partial sums
-// to add: measured faster at 8-9 active experts). 72 tiles: 3 slices of 6
-// stages make 216 items, where 4 slices of 4 make 288, two rounds of 4 for
-// some workgroups.
+// Gate/up split (split_stages) for every possible active-expert count n (the
+// count is only known on the device).
 static_assert(kMaxDim / kBK <= 255, "stages per slice fit a byte");
 void plan_gate_up(const Params &p, int G, UpPlan &up) {
   for (uint32_t &w : up.e2) w = 0;
@@ -1194,24 +1260,7 @@ void plan_gate_up(const Params &p, int G, UpPlan &up) {
   const int strips = ceil_div(p.I, kStripCols);
   const int planned = p.slices;
   for (int n = 0; n <= p.E; ++n) {
-    const int tiles = n * strips;
-    int best_blk = nblk, best_span = 0x7fffffff;
-    for (int sl = 2; sl <= planned; ++sl) {
-      const int b = ceil_div(nblk, sl);
-      const int span = ceil_div(tiles * ceil_div(nblk, b), G) * b;
-      if (span < best_span) {
-        best_span = span;
-        best_blk = b;
-      }
-    }
-    bool whole;
-    if (planned == 1)
-      whole = true;
-    else if (tiles <= G)
-      whole = 5 * tiles >= 3 * G;
-    else
-      whole = ceil_div(tiles, G) * nblk <= best_span + kSliceCost;
-    const int blk = whole ? nblk : best_blk;
+    const int blk = split_stages(n * strips, nblk, planned, G);
     const int slices = ceil_div(nblk, blk);
     up.e2[n >> 1] |= (uint32_t(blk) | uint32_t(slices) << 8) << (16 * (n & 1));
   }
@@ -1248,6 +1297,10 @@ int ffn_items(int B, int d, int E, int I, int k, const Workspace &plan) {
 }
 
 }  // namespace
+
+#ifdef MOE_PHASE_STAMPS
+uint64_t *g_phase_stamps = nullptr;
+#endif
 
 hipError_t expert_ffn_launchable(moe_dtype_t dt, int B, int d, int E, int I, int k, const Workspace &plan) {
   if (dt != MOE_BF16) return hipSuccess;
@@ -1288,7 +1341,11 @@ hipError_t launch_expert_ffn(const void *x, const void *w_gate, const void *w_up
     p.pair_token = r.pair_token;
     p.pair_slot = r.pair_slot;
     p.sync = reinterpret_cast<uint32_t *>(ws);
+#ifdef MOE_PHASE_STAMPS
+    p.stamps = g_phase_stamps;
+#endif
     p.grp_cnt = reinterpret_cast<uint32_t *>(ws + kGrpCntOffset);
+    p.tile_cnt = reinterpret_cast<uint32_t *>(ws + kTileCntOffset);
     p.n_dstrips = ceil_div(d, 2 * kStripCols);
     const int items = ffn_items(B, d, E, I, k, plan);
     // An expert has at most B tokens: A tiles of 16 * MTX rows cover them
@@ -1312,3 +1369,9 @@ hipError_t launch_expert_ffn(const void *x, const void *w_gate, const void *w_up
 }
 
 }  // namespace moe
+
+#ifdef MOE_PHASE_STAMPS
+// Measurement library only: where the next bf16 expert FFN launches record
+// their phase stamps (device pointer to 256 x 64 uint64, or NULL for none).
+extern "C" void moe_phase_stamps(void *stamps) { moe::g_phase_stamps = static_cast<uint64_t *>(stamps); }
+#endif

@@ -40,8 +40,9 @@ inline float lynx_bin_width(int E, int k) { return float(std::log(double(E) / do
 // (the same for every size of call, so that calls of different sizes may
 // share a workspace): the expert FFN's grid-barrier words (first 384 bytes),
 // the fused router + selection counter, the router's per-tile counters (up
-// to 256 tiles) and the FFN's per-(16-token group, 128-column strip of d)
-// counters, each of those on a 128-byte line of its own (atomics on one line
+// to 256 tiles), the FFN's per-(16-token group, 128-column strip of d)
+// counters, each of those on a 128-byte line of its own, and the FFN's
+// per-gate/up-tile slice counters (atomics on one line
 // are served one after another). All are zero before the workspace's first
 // use. Every call leaves the counters at zero; the barrier's release word
 // only grows. No other step writes them.
@@ -54,8 +55,14 @@ constexpr int kTokGroup = 16;                      // tokens per combine group
 constexpr int kTokGroups = kMaxB / kTokGroup;      // groups at B = kMaxB
 constexpr int kCntStride = 32;                     // uint32 words between group counters
 constexpr size_t kGrpCntOffset = kSyncBytes;       // [kMaxDim / 128 strips][kTokGroups] x 128 B
-constexpr size_t kCounterBytes =
+// FFN, sliced gate/up path: per gate/up tile (active expert, 64-column strip
+// of I), the d slices counted so far, each on a 64-byte piece of a line.
+// Tiles past kMaxTileCounters take the whole-d path (no counter needed).
+constexpr int kMaxTileCounters = 4096;
+constexpr int kTileCntStride = 16;                 // uint32 words between tile counters
+constexpr size_t kTileCntOffset =
     kGrpCntOffset + size_t(kMaxDim / (2 * kStripCols)) * kTokGroups * kCntStride * 4;
+constexpr size_t kCounterBytes = kTileCntOffset + size_t(kMaxTileCounters) * kTileCntStride * 4;
 
 // Workspace carve-up. Every segment starts on a 256-byte boundary.
 struct Workspace {

@@ -58,6 +58,15 @@ def _parse():
                          "the achievable HBM read rate on this GPU")
     ap.add_argument("--copy-calibration", type=float, default=0.0, metavar="MB",
                     help="run a plain device copy of MB megabytes 10 times and exit (counter scale)")
+    ap.add_argument("--phase-timeline", type=int, default=0, metavar="N",
+                    help="load the measurement library (expert FFN with phase stamps) and print, over N "
+                         "launches on rotating replicas, when each phase ends (p50 and max over "
+                         "workgroups, median over launches) and the weight bytes consumed per microsecond")
+    ap.add_argument("--write-traffic", default=None, metavar="DIR",
+                    help="no GPU: read the rocprofv3 counter CSVs of four passes under DIR (copy_fetch, "
+                         "copy_write, ffn_fetch, ffn_write; the copy of --copy-calibration MB and "
+                         "--ffn-only launches of the chosen workload) and write the traffic summary "
+                         "that the roofline's `traffic` field reads")
     return ap.parse_args()
 
 
@@ -103,9 +112,10 @@ class Case:
         self.L.moe_layer_decode(self.x, d["w_g"], self.bias, d["w_gate"], d["w_up"], d["w_down"],
                                 self.policy, self.logits, self.routing, self.y, self.ws)
 
-    def ffn(self, rep):
+    def ffn(self, rep, lib=None):
         d = self.replicas[rep]
-        self.L.moe_expert_ffn(self.x, d["w_gate"], d["w_up"], d["w_down"], self.routing, self.y, self.ws)
+        self.L.moe_expert_ffn(self.x, d["w_gate"], d["w_up"], d["w_down"], self.routing, self.y, self.ws,
+                              lib=lib)
 
 
 def _capture_chain(fn, first, count):
@@ -174,6 +184,88 @@ def _traffic(workload):
     if t.get("source_sha256") != _kernel_source_hash() or t.get("workload") != workload:
         return None
     return int(t["fetch_bytes"] + t["write_bytes"])
+
+
+def _counter_mean(dirpath, counter, kernel_substr):
+    """Mean per dispatch of one counter over the dispatches of kernels whose
+    name contains kernel_substr, from the rocprofv3 CSVs under dirpath."""
+    import csv
+    import glob
+    vals = []
+    for path in glob.glob(os.path.join(dirpath, "**", "*counter_collection.csv"), recursive=True):
+        with open(path, newline="") as f:
+            for row in csv.DictReader(f):
+                if row.get("Counter_Name") == counter and kernel_substr in row.get("Kernel_Name", ""):
+                    vals.append(float(row["Counter_Value"]))
+    if not vals:
+        raise SystemExit(f"no {counter} rows for {kernel_substr!r} under {dirpath}")
+    return float(np.mean(vals)), len(vals)
+
+
+def _write_traffic(dirpath, workload, copy_bytes, active_bytes):
+    """Traffic summary of the FFN kernel: FETCH_SIZE and WRITE_SIZE (KiB per
+    dispatch) scaled by what the same counters read for a plain copy that
+    reads and writes copy_bytes."""
+    cf, _ = _counter_mean(os.path.join(dirpath, "copy_fetch"), "FETCH_SIZE", "copyBuffer")
+    cw, _ = _counter_mean(os.path.join(dirpath, "copy_write"), "WRITE_SIZE", "copyBuffer")
+    ff, nf = _counter_mean(os.path.join(dirpath, "ffn_fetch"), "FETCH_SIZE", "ffn_kernel")
+    fw, nw = _counter_mean(os.path.join(dirpath, "ffn_write"), "WRITE_SIZE", "ffn_kernel")
+    sf, sw = copy_bytes / (cf * 1024.0), copy_bytes / (cw * 1024.0)
+    out = {"workload": workload, "kernel": "ffn_kernel", "source_sha256": _kernel_source_hash(),
+           "fetch_bytes": int(round(ff * 1024.0 * sf)), "write_bytes": int(round(fw * 1024.0 * sw)),
+           "fetch_size_kib_per_dispatch": ff, "write_size_kib_per_dispatch": fw,
+           "dispatches": [nf, nw], "copy_scale_fetch": sf, "copy_scale_write": sw,
+           "algorithmic_bytes": active_bytes}
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(out, f, indent=1)
+        f.write("\n")
+    print(json.dumps(out))
+
+
+PHASES = ["start", "routing lists in LDS", "first stage computed", "gate/up done", "first grid barrier passed",
+          "first down stages landed", "last down stage computed", "down rows stored", "rows counted",
+          "combine done", "end"]
+
+
+def _phase_timeline(c, launches):
+    """Phase ends of the expert FFN from the measurement library's stamps
+    (100 MHz clock, relative to the first workgroup's start), and the weight
+    bytes consumed per 1-us bin (32 KB of weights per stage)."""
+    import ctypes
+    import torch
+    from aware_expert_routing_amd import build as B
+    lib = c.L.load(B.PHASES_LIB)
+    lib.moe_phase_stamps.argtypes = [ctypes.c_void_p]
+    st = torch.zeros(256 * 64, dtype=torch.int64, device="cuda")
+    R = len(c.replicas)
+    for i in range(R):
+        c.ffn(i, lib=lib)
+    torch.cuda.synchronize()
+    lib.moe_phase_stamps(st.data_ptr())
+    runs = []
+    for i in range(launches):
+        st.zero_()
+        c.ffn((i * 7) % R, lib=lib)
+        torch.cuda.synchronize()
+        raw = st.view(256, 64).cpu().numpy().view(np.uint64)
+        used = raw[:, 0] > 0
+        raw = raw[used]
+        t0 = float(raw[:, 0].min())
+        t = (raw & np.uint64((1 << 63) - 1)).astype(np.float64)
+        runs.append(np.where(t > 0, (t - t0) * 0.01, np.nan))
+    lib.moe_phase_stamps(None)
+    torch.cuda.synchronize()
+    rows = []
+    for i, name in enumerate(PHASES):
+        col = [r[:, i] for r in runs]
+        n = int(np.median([np.isfinite(v).sum() for v in col]))
+        p50 = float(np.median([np.nanmedian(v) for v in col if np.isfinite(v).any()]))
+        mx = float(np.median([np.nanmax(v) for v in col if np.isfinite(v).any()]))
+        rows.append({"phase": name, "p50_us": round(p50, 2), "max_us": round(mx, 2), "workgroups": n})
+    stages = np.concatenate([r[:, 16:64].ravel() for r in runs])
+    stages = stages[np.isfinite(stages)]
+    hist = np.bincount(stages.astype(int)) * 32768 / len(runs) / 1e3  # GB/s in each 1-us bin
+    return {"phases": rows, "weight_GBps_per_us": [round(float(v)) for v in hist], "launches": launches}
 
 
 def _cpu_threads():
@@ -295,6 +387,19 @@ def _upload(inp, dtype):
 
 def main():
     args = _parse()
+    if args.write_traffic:
+        from aware_expert_routing_amd.workloads import CONFIGS
+        cfg = CONFIGS[args.config]
+        # The active set is the one the GPU run found: taken from the counter
+        # pass's own printout (bench.py --ffn-only), saved beside the CSVs.
+        with open(os.path.join(args.write_traffic, "ffn_only.json")) as f:
+            info = json.loads([ln for ln in f.read().splitlines() if ln.startswith('{"ffn_launches"')][-1])
+        pol = _policy_name(args.policy, args.k0, args.m, args.g)
+        workload = (f"{cfg.name} decode MoE layer, B={args.batch}, d={cfg.d}, E={cfg.E}, k={cfg.k}, "
+                    f"I={cfg.I}, policy {pol}")
+        _write_traffic(args.write_traffic, workload, int(args.copy_calibration * 1e6) // 4 * 4,
+                       info["active_expert_bytes"])
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: there is no multi-GPU path "
               f"(asked for --gpus {args.gpus}).", file=sys.stderr)
@@ -366,6 +471,15 @@ def main():
     cfg = CONFIGS[args.config]
     inp = make_layer(cfg, max(args.batch, max(cfg.batches)))
     dev = _upload(inp, cfg.dtype)
+    if args.phase_timeline:
+        c = Case(cfg, args.batch, args.policy, args.k0, args.m, inp, dev, args.rotate_bytes,
+                 args.g if args.policy == "hier" else 0)
+        tl = _phase_timeline(c, args.phase_timeline)
+        for r in tl["phases"]:
+            print(f"{r['phase']:28s} p50 {r['p50_us']:7.2f} us  max {r['max_us']:7.2f} us  ({r['workgroups']} workgroups)")
+        print("weight GB/s consumed per 1-us bin:", " ".join(f"{i}:{v}" for i, v in enumerate(tl["weight_GBps_per_us"])))
+        print(json.dumps({"n_active": c.n_active, "active_expert_bytes": c.active_bytes, **tl}), flush=True)
+        return
     if args.ffn_only:
         c = Case(cfg, args.batch, args.policy, args.k0, args.m, inp, dev, args.rotate_bytes,
                  args.g if args.policy == "hier" else 0)

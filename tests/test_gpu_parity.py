@@ -60,20 +60,23 @@ def _run_layer(cfg: LayerConfig, inp, dev, B: int, policy: str, k0: int, m: int,
 # Fixed counter region at the start of every workspace (byte offsets): barrier
 # count (0), release word (128), error word (256), router + selection counter
 # (384), router tile counters (512..1535), per-(strip, 16-token group)
-# counters (from 2048: 128 strips x 16 groups, 128 bytes each).
+# counters (from 2048: 128 strips x 16 groups, 128 bytes each), per gate/up
+# tile slice counters (then 4096 of them, 64 bytes each).
 _GRP_CNT = (2048, 2048 + 128 * 16 * 128)
+_TILE_CNT = (_GRP_CNT[1], _GRP_CNT[1] + 4096 * 64)
 
 
 def _assert_sync_words_clear(ws):
     """The FFN's grid-barrier count returns to zero, its error word stays
     zero (no bounded wait ran out), and every counter (router + selection,
-    router tiles, per-group strips) is back at zero."""
-    words = ws[:_GRP_CNT[1]].view(torch.int32).cpu().numpy()
+    router tiles, per-group strips, gate/up tiles) is back at zero."""
+    words = ws[:_TILE_CNT[1]].view(torch.int32).cpu().numpy()
     assert words[0] == 0, f"barrier count left at {words[0]}"
     assert words[64] == 0, "a bounded wait exceeded its limit"
     assert words[96] == 0, "the router + selection counter was left non-zero"
     assert not words[128:384].any(), "a router tile counter was left non-zero"
     assert not words[_GRP_CNT[0] // 4:_GRP_CNT[1] // 4].any(), "a per-group counter was left non-zero"
+    assert not words[_TILE_CNT[0] // 4:_TILE_CNT[1] // 4].any(), "a gate/up tile counter was left non-zero"
 
 
 def _oracle(cfg, inp, B, policy, k0, m, tokens=None, g=0):
