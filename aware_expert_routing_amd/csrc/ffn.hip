@@ -30,6 +30,7 @@
 //     results are reproducible).
 // float32 path (small layers): plain dot products, 16 row groups per column.
 #include <atomic>
+#include <type_traits>
 
 #include "moe_internal.h"
 
@@ -182,6 +183,15 @@ __device__ __forceinline__ float4 ld_dev4(__amdgpu_buffer_rsrc_t r, uint32_t off
   return make_float4(v[0], v[1], v[2], v[3]);
 }
 
+// Reads v at this point (an empty asm with v as input), so that the compiler
+// waits here for the load that wrote it. Cold code inside the stage loop
+// loads values that it may then read only on some paths; a register whose
+// load the compiler cannot see completed on every path stays pending around
+// the loop, and the compiler then waits for it (and for every weight copy
+// issued before it) wherever the stage loop reuses that register.
+__device__ __forceinline__ void consume(float v) { asm volatile("" ::"v"(v)); }
+__device__ __forceinline__ void consume(float4 v) { asm volatile("" ::"v"(v.x), "v"(v.y), "v"(v.z), "v"(v.w)); }
+
 // s_waitcnt vmcnt(N) lgkmcnt(0), then s_barrier. Compiler barriers keep LDS
 // accesses on their side of the s_barrier.
 template <int N>
@@ -307,7 +317,6 @@ struct Params {
   uint16_t *h;                // [P][I] SiLU(g) * u by pair
   float *part;                // [P][d] down-projection rows by token slot t*k+j
   uint16_t *y;                // [B][d]
-  const int32_t *ids;         // [B][k]
   const float *w;             // [B][k]
   const int32_t *pair_token;  // [P]
   const int32_t *pair_slot;   // [P]
@@ -318,6 +327,7 @@ struct Params {
   uint32_t *grp_cnt;          // per (strip, token group): slots counted, one 128-byte line each
   uint32_t *tile_cnt;         // per gate/up tile (sliced path): d slices counted
   int n_dstrips;              // 128-column strips of d
+  int dslices, dslice_rows;   // down reduction (I) slices (1: all of I)
 };
 
 // By active-expert count: gate/up stages of kBK rows per d slice (all of d
@@ -386,10 +396,11 @@ struct Stream {
     } else {
       const int jd = c.item - c.n_up;
       a = jd / c.per_dn;
-      c.strip = jd - a * c.per_dn;
-      c.ks = 0;
-      c.row0 = 0;
-      c.nrows = p.I;
+      const int rem = jd - a * c.per_dn;
+      c.strip = rem / p.dslices;
+      c.ks = rem - c.strip * p.dslices;
+      c.row0 = c.ks * p.dslice_rows;
+      c.nrows = min(p.dslice_rows, p.I - c.row0);
     }
     c.e = __builtin_amdgcn_readfirstlane(lds_i16(meta + kMetaAct + 2 * a));
     c.p0 = __builtin_amdgcn_readfirstlane(lds_i16(meta + kMetaOff + 2 * a));
@@ -410,29 +421,31 @@ struct Stream {
 
   // Byte offset of the A row this lane copies for its copy h (MTX copies per
   // wave, one 16-row tile each, all at k-step `wave` of the stage).
+  template <bool UP>
   __device__ __forceinline__ uint32_t xvoff(const Cursor &c, int h) const {
     const int m = 16 * h + (lane >> 2);
     const int T = tp(c);
     const int pr = c.p0 + c.pass * kMaxTok + (m < T ? m : T - 1);
     const int lc = (lane & 3) ^ swz_x(m);
     const uint32_t kofs = uint32_t(wave * 32 + lc * 8);
-    if (c.up) return (uint32_t(lds_u8(meta + kMetaTok + pr)) * uint32_t(p.d) + kofs) * 2u;
+    if constexpr (UP) return (uint32_t(lds_u8(meta + kMetaTok + pr)) * uint32_t(p.d) + kofs) * 2u;
     return (uint32_t(pr) * uint32_t(p.I) + kofs) * 2u;
   }
 
   // The A-tile copies of stage c (MTX per wave): x rows by token for gate/up,
   // h rows by pair for down (device scope: other workgroups wrote h).
+  template <bool UP>
   __device__ __forceinline__ void issue_a(const Cursor &c, unsigned char *slot) const {
     unsigned char *dst = slot + 2 * kWTile + wave * S::kXSub;
     const uint32_t xsoff = uint32_t(c.row0 + c.kst * kBK) * 2u;
-    if (c.up) {
+    if constexpr (UP) {
       const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.x, uint32_t(p.B) * uint32_t(p.d) * 2u);
 #pragma unroll
-      for (int h = 0; h < MTX; ++h) dma16(ra, dst + h * 1024, xvoff(c, h), xsoff);
+      for (int h = 0; h < MTX; ++h) dma16(ra, dst + h * 1024, xvoff<true>(c, h), xsoff);
     } else {
       const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.h, uint32_t(p.P) * uint32_t(p.I) * 2u);
 #pragma unroll
-      for (int h = 0; h < MTX; ++h) dma16<kPolicyDevice>(ra, dst + h * 1024, xvoff(c, h), xsoff);
+      for (int h = 0; h < MTX; ++h) dma16<kPolicyDevice>(ra, dst + h * 1024, xvoff<false>(c, h), xsoff);
     }
   }
 
@@ -443,7 +456,7 @@ struct Stream {
     const __amdgpu_buffer_rsrc_t r = make_rsrc(p.W[2] + base, uint32_t(p.I) * uint32_t(p.d) * 2u);
 #pragma unroll
     for (int mat = 0; mat < 2; ++mat) {
-      const uint32_t soff = (uint32_t(c.kst * kBK) * uint32_t(p.d) +
+      const uint32_t soff = (uint32_t(c.row0 + c.kst * kBK) * uint32_t(p.d) +
                              uint32_t((2 * c.strip + mat) * kStripCols)) * 2u;
 #pragma unroll
       for (int h = 0; h < 4; ++h) {
@@ -454,11 +467,12 @@ struct Stream {
     }
   }
 
-  // Issues half of this wave's copies of stage c into `slot`: half 0 the
-  // first weight tile and the A tile, half 1 the second weight tile
-  // (S::kCopies per wave in all).
+  // Issues half of this wave's copies of stage c (a gate/up stage when UP,
+  // else a down stage) into `slot`: half 0 the first weight tile and the A
+  // tile, half 1 the second weight tile (S::kCopies per wave in all).
+  template <bool UP>
   __device__ __forceinline__ void issue_half(const Cursor &c, unsigned char *slot, int half) const {
-    if (c.up) {
+    if constexpr (UP) {
       const size_t base = (size_t(c.e) * p.d + c.row0) * p.I;
       const uint32_t wbytes = uint32_t(c.nrows) * uint32_t(p.I) * 2u;
       const uint32_t soff =
@@ -469,17 +483,17 @@ struct Stream {
     } else {
       const size_t base = size_t(c.e) * p.I * p.d;
       const __amdgpu_buffer_rsrc_t r = make_rsrc(p.W[2] + base, uint32_t(p.I) * uint32_t(p.d) * 2u);
-      const uint32_t soff = (uint32_t(c.kst * kBK) * uint32_t(p.d) +
+      const uint32_t soff = (uint32_t(c.row0 + c.kst * kBK) * uint32_t(p.d) +
                              uint32_t((2 * c.strip + half) * kStripCols)) * 2u;
 #pragma unroll
       for (int h = 0; h < 4; ++h) dma16<kPolicyStream>(r, slot + half * kWTile + (wave + 4 * h) * 1024, wv_dn[h], soff);
     }
-    if (half == 0) issue_a(c, slot);
+    if (half == 0) issue_a<UP>(c, slot);
   }
-  // Issues every copy of stage c into `slot`.
-  __device__ __forceinline__ void issue(const Cursor &c, unsigned char *slot) const {
-    issue_half(c, slot, 0);
-    issue_half(c, slot, 1);
+  // Issues every copy of gate/up stage c into `slot`.
+  __device__ __forceinline__ void issue_up(const Cursor &c, unsigned char *slot) const {
+    issue_half<true>(c, slot, 0);
+    issue_half<true>(c, slot, 1);
   }
 };
 
@@ -637,14 +651,14 @@ __device__ __forceinline__ void compute_stage(uint32_t slot, const uint32_t (&tr
 // Stores the accumulators of the pass that just ended: the gate and up partial
 // sums of slice ks by pair, or two 64-column tiles of the down projection by
 // token slot.
-// A pass has at most 16 * MTX tokens.
-template <int MTX>
+// A pass has at most 16 * MTX tokens. UP: c is a gate/up item.
+template <int MTX, bool UP>
 __device__ __forceinline__ void epilogue(const Cursor &c, const Params &p, uint32_t meta, int wave,
                                          int lane, Acc &acc) {
   const int g = lane >> 4, j = lane & 15;
   const int T = min(kMaxTok, c.T - c.pass * kMaxTok);
   const int pbase = c.p0 + c.pass * kMaxTok;
-  if (c.up && p.slices == 1) {
+  if (UP && p.slices == 1) {
     // The whole reduction is in the accumulators: h = SiLU(g) * u by pair.
     const int col = c.strip * kStripCols + 16 * wave + j;
     if (col < p.I) {
@@ -665,7 +679,7 @@ __device__ __forceinline__ void epilogue(const Cursor &c, const Params &p, uint3
   }
   float *dst0, *dst1;
   int col0, col1, ld;
-  if (c.up) {
+  if constexpr (UP) {
     ld = p.I;
     col0 = col1 = c.strip * kStripCols + 16 * wave + j;
     dst0 = p.gpart + size_t(c.ks * 2) * p.P * p.I;
@@ -674,7 +688,7 @@ __device__ __forceinline__ void epilogue(const Cursor &c, const Params &p, uint3
     ld = p.d;
     col0 = 2 * c.strip * kStripCols + 16 * wave + j;
     col1 = col0 + kStripCols;
-    dst0 = dst1 = p.part;
+    dst0 = dst1 = p.part + size_t(c.ks) * p.P * p.d;
   }
   const bool ok0 = col0 < ld, ok1 = col1 < ld;
 #pragma unroll
@@ -683,7 +697,7 @@ __device__ __forceinline__ void epilogue(const Cursor &c, const Params &p, uint3
     for (int i = 0; i < 4; ++i) {
       const int m = 16 * t4 + 4 * g + i;
       if (m < T) {
-        const size_t row = size_t(c.up ? pbase + m : lds_i16(meta + kMetaRow + 2 * (pbase + m))) * ld;
+        const size_t row = size_t(UP ? pbase + m : lds_i16(meta + kMetaRow + 2 * (pbase + m))) * ld;
         if (ok0) st_dev(dst0 + row + col0, acc.mf[0][t4][i]);
         if (ok1) st_dev(dst1 + row + col1, acc.mf[1][t4][i]);
       }
@@ -711,27 +725,35 @@ __device__ __forceinline__ void finish_up(const Cursor &c, const Params &p, int 
   __syncthreads();
   if (!*flag) return;
   const uint32_t blk = uint32_t(p.P) * uint32_t(p.I) * 4u;  // bytes of one [P][I] block
+  const __amdgpu_buffer_rsrc_t r = make_rsrc(p.gpart, uint32_t(p.slices) * 2u * blk);
   const int col0 = c.strip * kStripCols;
   for (int u = threadIdx.x; u < c.T * (kStripCols / 4); u += kThreads) {
     const int m = u / (kStripCols / 4);
     const int col = col0 + (u - m * (kStripCols / 4)) * 4;  // I % 8 == 0: col < I means col + 3 < I
     if (col >= p.I) continue;
     const uint32_t off = (uint32_t(c.p0 + m) * uint32_t(p.I) + uint32_t(col)) * 4u;
+    // Slices past p.slices load slice 0 again and are masked out: every
+    // load is unconditional and read at once (consume).
     float4 gv[kUpMaxSlices], uv[kUpMaxSlices];
 #pragma unroll
-    for (int s = 0; s < kUpMaxSlices; ++s) {
-      if (s < p.slices) {
-        gv[s] = ld_dev4(make_rsrc(p.gpart + size_t(s * 2 + 0) * p.P * p.I, blk), off);
-        uv[s] = ld_dev4(make_rsrc(p.gpart + size_t(s * 2 + 1) * p.P * p.I, blk), off);
-      }
+    for (int sl = 0; sl < kUpMaxSlices; ++sl) {
+      const uint32_t so = uint32_t(sl < p.slices ? sl : 0) * 2u * blk;
+      gv[sl] = ld_dev4(r, off + so);
+      uv[sl] = ld_dev4(r, off + so + blk);
+    }
+#pragma unroll
+    for (int sl = 0; sl < kUpMaxSlices; ++sl) {
+      consume(gv[sl]);
+      consume(uv[sl]);
     }
     float4 g = make_float4(0, 0, 0, 0), v = make_float4(0, 0, 0, 0);
 #pragma unroll
-    for (int s = 0; s < kUpMaxSlices; ++s) {
-      if (s < p.slices) {
-        g.x += gv[s].x; g.y += gv[s].y; g.z += gv[s].z; g.w += gv[s].w;
-        v.x += uv[s].x; v.y += uv[s].y; v.z += uv[s].z; v.w += uv[s].w;
-      }
+    for (int sl = 0; sl < kUpMaxSlices; ++sl) {
+      const bool in = sl < p.slices;
+      const float4 a = in ? gv[sl] : make_float4(0, 0, 0, 0);
+      const float4 b = in ? uv[sl] : make_float4(0, 0, 0, 0);
+      g.x += a.x; g.y += a.y; g.z += a.z; g.w += a.w;
+      v.x += b.x; v.y += b.y; v.z += b.z; v.w += b.w;
     }
     const uint64_t o = uint64_t(f32_to_bf16(silu(g.x) * v.x)) |
                        (uint64_t(f32_to_bf16(silu(g.y) * v.y)) << 16) |
@@ -765,10 +787,12 @@ __device__ __forceinline__ uint32_t xcd_id() { return __builtin_amdgcn_s_getreg(
 
 // y over 128-column strip `strip` for the tokens of group grp: thread i takes
 // token 16*grp + i/16 and columns 8*(i%16) .. +7 of the strip, adding
-// w[t,j] * part[t*k+j] in slot order (empty slots skipped). Slots are taken
-// eight at a time with every load of a round issued before the first use.
-// The rows were stored with device-scope stores, which also update the L2 of
-// the storing XCD; when every row of the group's strip came from this
+// w[t,j] * (part[0][t*k+j] + part[1][t*k+j] + ...) (the I slices' rows, in
+// slice order) in slot order over the token's filled slots (fill[t] of
+// them; a routing's empty slots trail its filled ones). Up to eight rows are
+// loaded per round, every load of a round issued before the first use. The
+// rows were stored with device-scope stores, which also update the L2 of the
+// storing XCD; when every row of the group's strip came from this
 // workgroup's XCD (`local`), they are read through that L2, else from the
 // device-coherent level.
 static_assert(kThreads == kTokGroup * (2 * kStripCols / 8), "one thread per token and 8 columns");
@@ -777,39 +801,68 @@ __device__ __forceinline__ float4 ld_part4(__amdgpu_buffer_rsrc_t r, uint32_t of
                           : __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, int(off), 0, kPolicyDevice));
   return make_float4(v[0], v[1], v[2], v[3]);
 }
-__device__ __forceinline__ void combine_group(const Params &p, int grp, int strip, bool local) {
+__device__ __forceinline__ void combine_group(const Params &p, const uint32_t *fill, int grp, int strip,
+                                              bool local) {
   const int t = grp * kTokGroup + (threadIdx.x >> 4);
   const int col = strip * 2 * kStripCols + (threadIdx.x & 15) * 8;
   if (t >= p.B || col >= p.d) return;
-  const __amdgpu_buffer_rsrc_t rp = make_rsrc(p.part, uint32_t(p.P) * uint32_t(p.d) * 4u);
+  const int ds = p.dslices;
+  const int nf = int(fill[t]);
+  const int per_round = max(1, 8 / ds);  // slots per round
+  const __amdgpu_buffer_rsrc_t rp = make_rsrc(p.part, uint32_t(ds) * uint32_t(p.P) * uint32_t(p.d) * 4u);
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  for (int j0 = 0; j0 < p.k; j0 += 8) {
-    int id[8];
+  for (int j0 = 0; j0 < nf; j0 += per_round) {
+    const int nq = min(per_round, nf - j0) * ds;  // rows this round
+    // Row q of the round: slot j0 + q / ds, I slice q % ds. Rows past nq
+    // load row q = 0 again and are masked out: every load is unconditional
+    // and read at once (consume).
     float w[8];
     float4 v[8][2];
+    int jj = 0, ks = 0;  // q / ds and q % ds
 #pragma unroll
-    for (int jj = 0; jj < 8; ++jj) {
-      const int j = j0 + jj;
-      if (j < p.k) {
-        const int slot = t * p.k + j;
-        id[jj] = p.ids[slot];
-        w[jj] = p.w[slot];
-        const uint32_t off = (uint32_t(slot) * uint32_t(p.d) + uint32_t(col)) * 4u;
-        v[jj][0] = ld_part4(rp, off, local);
-        v[jj][1] = ld_part4(rp, off + 16u, local);
+    for (int q = 0; q < 8; ++q) {
+      const bool in = q < nq;
+      const int slot = t * p.k + j0 + (in ? jj : 0);
+      w[q] = p.w[slot];
+      const uint32_t off = ((uint32_t(in ? ks : 0) * uint32_t(p.P) + uint32_t(slot)) * uint32_t(p.d) + uint32_t(col)) * 4u;
+      v[q][0] = ld_part4(rp, off, local);
+      v[q][1] = ld_part4(rp, off + 16u, local);
+      if (++ks == ds) {
+        ks = 0;
+        ++jj;
       }
     }
 #pragma unroll
-    for (int jj = 0; jj < 8; ++jj) {
-      if (j0 + jj < p.k && id[jj] >= 0) {
-        acc[0] = fmaf(w[jj], v[jj][0].x, acc[0]);
-        acc[1] = fmaf(w[jj], v[jj][0].y, acc[1]);
-        acc[2] = fmaf(w[jj], v[jj][0].z, acc[2]);
-        acc[3] = fmaf(w[jj], v[jj][0].w, acc[3]);
-        acc[4] = fmaf(w[jj], v[jj][1].x, acc[4]);
-        acc[5] = fmaf(w[jj], v[jj][1].y, acc[5]);
-        acc[6] = fmaf(w[jj], v[jj][1].z, acc[6]);
-        acc[7] = fmaf(w[jj], v[jj][1].w, acc[7]);
+    for (int q = 0; q < 8; ++q) {
+      consume(w[q]);
+      consume(v[q][0]);
+      consume(v[q][1]);
+    }
+    float4 s0 = make_float4(0.f, 0.f, 0.f, 0.f), s1 = make_float4(0.f, 0.f, 0.f, 0.f);
+    ks = 0;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const bool in = q < nq;
+      const bool last = ++ks == ds;  // the slot's last I slice
+      if (last) ks = 0;
+      const float4 a = in ? v[q][0] : make_float4(0.f, 0.f, 0.f, 0.f);
+      const float4 b = in ? v[q][1] : make_float4(0.f, 0.f, 0.f, 0.f);
+      const float wj = in ? w[q] : 0.f;
+      s0.x += a.x; s0.y += a.y; s0.z += a.z; s0.w += a.w;
+      s1.x += b.x; s1.y += b.y; s1.z += b.z; s1.w += b.w;
+      if (in && last) {
+        acc[0] = fmaf(wj, s0.x, acc[0]);
+        acc[1] = fmaf(wj, s0.y, acc[1]);
+        acc[2] = fmaf(wj, s0.z, acc[2]);
+        acc[3] = fmaf(wj, s0.w, acc[3]);
+        acc[4] = fmaf(wj, s1.x, acc[4]);
+        acc[5] = fmaf(wj, s1.y, acc[5]);
+        acc[6] = fmaf(wj, s1.z, acc[6]);
+        acc[7] = fmaf(wj, s1.w, acc[7]);
+      }
+      if (last) {
+        s0 = make_float4(0.f, 0.f, 0.f, 0.f);
+        s1 = make_float4(0.f, 0.f, 0.f, 0.f);
       }
     }
   }
@@ -857,7 +910,7 @@ __device__ __forceinline__ void finish_down(const Cursor &c, const Params &p, un
       const uint64_t now = __hip_atomic_fetch_add(group_counter(p, grp, c.strip), add,
                                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + add;
       const uint64_t s0 = now & 0xFFFFu, s1 = (now >> 16) & 0xFFFFu, s2 = now >> 32;
-      mine = s0 == gfill[grp];
+      mine = s0 == gfill[grp] * uint32_t(p.dslices);
       local = mine && s1 * s1 == s0 * s2 && s1 == s0 * x;
     }
     const unsigned long long b = __ballot(mine);
@@ -869,7 +922,7 @@ __device__ __forceinline__ void finish_down(const Cursor &c, const Params &p, un
   const int n = *n_last;
   for (int q = 0; q < n; ++q) {
     const int grp = last[q] & 0xFFFF;
-    combine_group(p, grp, c.strip, (last[q] >> 16) != 0);
+    combine_group(p, reinterpret_cast<const uint32_t *>(meta + kMetaFill), grp, c.strip, (last[q] >> 16) != 0);
     if (threadIdx.x == 0)
       __hip_atomic_store(group_counter(p, grp, c.strip), uint64_t(0), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
@@ -925,7 +978,7 @@ __device__ __forceinline__ void change_to_down(const Params &p, const Stream<MTX
   barrier_no_wait();
   MOE_STAMP(4);
   for (int n = 0; n < kD && prod.valid; ++n) {
-    st.issue_a(prod, stages + ((first + n) % kS) * S::kSlot);
+    st.template issue_a<false>(prod, stages + ((first + n) % kS) * S::kSlot);
     st.advance(prod);
     ++issued;
   }
@@ -1039,11 +1092,21 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_kernel(Params p, const UpPlan
       p.slice_rows = blk * kBK;
     }
   }
+  // The down split: as many I slices, up to the planned number (whose
+  // partial rows the workspace holds), as leave every down item a workgroup
+  // of its own (small active sets), in whole stages.
+  {
+    const int nbi = (p.I + kBK - 1) / kBK;
+    const int ds = max(1, min(p.dslices, int(gridDim.x) / max(nact * p.n_dstrips, 1)));
+    const int blk = (nbi + ds - 1) / ds;
+    p.dslices = (nbi + blk - 1) / blk;
+    p.dslice_rows = blk * kBK;
+  }
 
   const Stream<MTX> st(p, lds_addr(meta));
   Cursor cons;
   cons.per_up = ((p.I + kStripCols - 1) / kStripCols) * p.slices;
-  cons.per_dn = (p.d + 2 * kStripCols - 1) / (2 * kStripCols);
+  cons.per_dn = p.n_dstrips * p.dslices;
   cons.n_up = nact * cons.per_up;
   cons.n_items = cons.n_up + nact * cons.per_dn;
   cons.item = blockIdx.x;
@@ -1055,7 +1118,7 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_kernel(Params p, const UpPlan
   int issued = 0;
   for (int s = 0; s < kD; ++s) {
     if (!prod.valid || !prod.up) break;
-    st.issue(prod, stages + s * S::kSlot);
+    st.issue_up(prod, stages + s * S::kSlot);
     ++issued;
     st.advance(prod);
   }
@@ -1063,14 +1126,13 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_kernel(Params p, const UpPlan
   Acc acc;
   clear(acc);
   const uint32_t base = lds_addr(stages);
-  bool h_ready = false;
-  for (int s = 0; cons.valid; ++s) {
-    if (!cons.up && !h_ready) {
-      change_to_down<MTX>(p, st, prod, issued, s, stages, rel_base);
-      h_ready = true;
-    }
-    // Stage s must have landed; the stages issued after it may stay in flight
-    // (S::kCopies copies per wave each).
+  // One stage of the consumer: stage s must have landed (the stages issued
+  // after it may stay in flight, S::kCopies copies per wave each); every wave
+  // is then past stage s-1, so its slot takes stage s+kD, whose copies are
+  // issued in two halves during the compute of stage s. The gate/up and down
+  // phases run in loops of their own (UP), each with only its own code.
+  auto stage = [&](int s, auto up_tag) {
+    constexpr bool UP = decltype(up_tag)::value;
     const int newer = issued - s - 1;
     switch (newer < kD - 1 ? newer : kD - 1) {
       case 0: wait_barrier<0>(); break;
@@ -1078,14 +1140,13 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_kernel(Params p, const UpPlan
       case 2: wait_barrier<(kD - 1 >= 2 ? 2 : 0) * S::kCopies>(); break;
       default: wait_barrier<(kD - 1 >= 3 ? 3 : 0) * S::kCopies>(); break;
     }
-    // Every wave is past stage s-1, so its slot takes stage s+kD, whose
-    // copies are issued in two halves during the compute of stage s.
-    MOE_STAGE_STAMP(s, !cons.up);
-    const bool fill = prod.valid && (prod.up || h_ready);
+    MOE_STAGE_STAMP(s, !UP);
+    // Gate/up: the producer stops at the first down stage (change_to_down).
+    const bool fill = prod.valid && (!UP || prod.up);
     unsigned char *fslot = stages + ((s + kD) % kS) * S::kSlot;
     compute_stage<MTX>(base + uint32_t((s % kS) * S::kSlot), st.trc, st.xrd, st.tp(cons), acc,
                        [&](int half) {
-                         if (fill) st.issue_half(prod, fslot, half);
+                         if (fill) st.template issue_half<UP>(prod, fslot, half);
                        });
     if (s == 0) MOE_STAMP(2);
     if (fill) {
@@ -1093,15 +1154,21 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_kernel(Params p, const UpPlan
       st.advance(prod);
     }
     if (cons.kst == cons.nst - 1) {
-      epilogue<MTX>(cons, p, st.meta, st.wave, st.lane, acc);
+      epilogue<MTX, UP>(cons, p, st.meta, st.wave, st.lane, acc);
       clear(acc);
-      if (!cons.up) finish_down(cons, p, meta, st.wave, st.lane);
-      else if (p.slices > 1 && (cons.pass + 1) * kMaxTok >= cons.T)
-        finish_up(cons, p, reinterpret_cast<int *>(meta + kMetaNLast));
+      if constexpr (UP) {
+        if (p.slices > 1 && (cons.pass + 1) * kMaxTok >= cons.T)
+          finish_up(cons, p, reinterpret_cast<int *>(meta + kMetaNLast));
+      } else {
+        finish_down(cons, p, meta, st.wave, st.lane);
+      }
     }
     st.advance(cons);
-  }
-  if (!h_ready) change_to_down<MTX>(p, st, prod, issued, 0, stages, rel_base);  // no down items here
+  };
+  int s = 0;
+  for (; cons.valid && cons.up; ++s) stage(s, std::true_type{});
+  change_to_down<MTX>(p, st, prod, issued, s, stages, rel_base);
+  for (; cons.valid; ++s) stage(s, std::false_type{});
   MOE_STAMP(10);
 }
 
@@ -1293,7 +1360,7 @@ hipError_t launch_ffn(int items, Params &p, const moe_routing_t &r, hipStream_t 
 int ffn_items(int B, int d, int E, int I, int k, const Workspace &plan) {
   const int P = B * k;
   const int max_active = E < P ? E : P;
-  return max_active * (ceil_div(I, kStripCols) * plan.up_slices + ceil_div(d, 2 * kStripCols));
+  return max_active * (ceil_div(I, kStripCols) * plan.up_slices + ceil_div(d, 2 * kStripCols) * plan.dn_slices);
 }
 
 }  // namespace
@@ -1336,7 +1403,6 @@ hipError_t launch_expert_ffn(const void *x, const void *w_gate, const void *w_up
     p.h = reinterpret_cast<uint16_t *>(ws + plan.h);
     p.part = part;
     p.y = static_cast<uint16_t *>(y);
-    p.ids = r.topk_ids;
     p.w = r.topk_w;
     p.pair_token = r.pair_token;
     p.pair_slot = r.pair_slot;
@@ -1347,6 +1413,7 @@ hipError_t launch_expert_ffn(const void *x, const void *w_gate, const void *w_up
     p.grp_cnt = reinterpret_cast<uint32_t *>(ws + kGrpCntOffset);
     p.tile_cnt = reinterpret_cast<uint32_t *>(ws + kTileCntOffset);
     p.n_dstrips = ceil_div(d, 2 * kStripCols);
+    p.dslices = plan.dn_slices;
     const int items = ffn_items(B, d, E, I, k, plan);
     // An expert has at most B tokens: A tiles of 16 * MTX rows cover them
     // (experts with more than 64 tokens take several passes).

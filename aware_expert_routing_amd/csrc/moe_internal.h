@@ -27,6 +27,13 @@ constexpr int kStripCols = 64;
 constexpr int kUpMaxSlices = 8;     // reduction (d) slices of the gate/up product
 constexpr int kUpSliceMin = 512;    // rows per slice before the slice count grows
 constexpr int kStageRows = 128;     // weight rows staged in LDS per pipeline stage
+constexpr int kDnMaxSlices = 8;     // reduction (I) slices of the down product
+// Partial-sum bytes beyond which the slice counts stop growing: gate/up takes
+// up to one slice per stage while its partial sums fit kUpPartBudget (else
+// one per kUpSliceMin rows of d), down up to one per stage of I while its
+// partial rows fit kDnPartBudget.
+constexpr size_t kUpPartBudget = size_t(16) << 20;
+constexpr size_t kDnPartBudget = size_t(8) << 20;
 
 inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
@@ -69,25 +76,34 @@ struct Workspace {
   size_t router_part;  // float [tiles][router_slices][16 x 16] partial logit tiles
   size_t up_part;      // float [up_slices][2][B*k][I]   (gate, up partial sums)
   size_t h;            // bf16 or float [B*k][I]
-  size_t down_part;    // float [B*k][d], one row per (expert, token) pair
+  size_t down_part;    // float [dn_slices][B*k][d], one row per (I slice, expert-token pair)
   size_t pair_of_slot; // int32 [B*k]: pair index of token slot t*k+j
   size_t total;
   int router_slices;
   int up_slices;
   int up_slice_rows;
+  int dn_slices;       // most I slices of the down product (the kernel may use fewer)
 };
 
 inline Workspace plan_workspace(int B, int d, int E, int I, int k, moe_dtype_t dt) {
   Workspace w{};
   w.router_slices = ceil_div(d, kRouterRows);
   const size_t router_tiles = size_t(ceil_div(E, kRouterTile)) * ceil_div(B, kRouterTile);
+  const size_t P = size_t(B) * size_t(k);
   int slices = ceil_div(d, kUpSliceMin);
+  const size_t up_slice_bytes = 2 * P * size_t(I) * sizeof(float);
+  const int by_budget = int(kUpPartBudget / up_slice_bytes);
+  if (by_budget > slices) slices = by_budget < ceil_div(d, kStageRows) ? by_budget : ceil_div(d, kStageRows);
   if (slices > kUpMaxSlices) slices = kUpMaxSlices;
   int rows = ceil_div(d, slices);
   rows = ceil_div(rows, kStageRows) * kStageRows;
   w.up_slices = ceil_div(d, rows);
   w.up_slice_rows = rows;
-  const size_t P = size_t(B) * size_t(k);
+  const size_t dn_slice_bytes = P * size_t(d) * sizeof(float);
+  int dn = int(kDnPartBudget / dn_slice_bytes);
+  if (dn > ceil_div(I, kStageRows)) dn = ceil_div(I, kStageRows);
+  if (dn > kDnMaxSlices) dn = kDnMaxSlices;
+  w.dn_slices = (dt == MOE_BF16 && dn > 1) ? dn : 1;
   const size_t esz = (dt == MOE_BF16) ? 2 : 4;
   size_t off = kCounterBytes;
   w.router_part = off;
@@ -97,7 +113,7 @@ inline Workspace plan_workspace(int B, int d, int E, int I, int k, moe_dtype_t d
   w.h = off;
   off = align256(off + P * I * esz);
   w.down_part = off;
-  off = align256(off + P * size_t(d) * sizeof(float));
+  off = align256(off + size_t(w.dn_slices) * P * size_t(d) * sizeof(float));
   w.pair_of_slot = off;
   off = align256(off + P * sizeof(int32_t));
   w.total = off;
