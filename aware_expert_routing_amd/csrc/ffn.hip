@@ -280,28 +280,43 @@ __device__ __forceinline__ void grid_barrier_wave(uint32_t *sync, uint32_t base,
   }
 }
 
-// Stages per gate/up item for `tiles` gate/up tiles (active expert, 64-column
-// strip of I) of nblk stages each on G workgroups: nblk (whole-d tiles, h
-// formed in the epilogue) or the stages of one of 2 up to `planned` d slices
-// (the partial sums the workspace holds). The cost of a split is its busiest
-// workgroup's items times (stages per item + kFinishStages): after each
-// sliced item a workgroup waits for its partial sums to be stored and
-// counted, and the workgroup completing a tile forms its h, a few round trips
-// to memory under full load (about four stages' time, measured). The
-// cheapest wins, ties to whole tiles and then to fewer slices (fewer partial
-// sums to store and add). More tiles than tile counters take whole d.
+// Gate/up split for `tiles` gate/up tiles (active expert, 64-column strip of
+// I) of nblk stages each on G workgroups, as an UpPlan entry: stages per
+// slice | slices << 8 | kUpMixed. Three forms:
+//   whole    every tile takes all of d (h formed in its epilogue);
+//   sliced   every tile is split into 2 up to `planned` d slices (the
+//            partial sums the workspace holds);
+//   mixed    the tiles of whole rounds of the grid are taken whole and the
+//            rest (fewer than G) are split so that every slice item gets a
+//            workgroup of its own in the last round.
+// The cost of a form is its busiest workgroup's stages, plus kFinishStages
+// per sliced item: after a sliced item a workgroup waits for its partial sums
+// to be stored and counted, and the workgroup completing a tile forms its h,
+// a few round trips to memory under full load (about four stages' time,
+// measured). The cheapest wins, ties to whole tiles and then to fewer slices
+// (fewer partial sums to store and add). More split tiles than tile
+// counters are not split.
 constexpr int kFinishStages = 4;
-__host__ __device__ inline int split_stages(int tiles, int nblk, int planned, int G) {
-  int best = nblk;
+constexpr uint32_t kUpMixed = 1u << 15;
+inline uint32_t plan_split(int tiles, int nblk, int planned, int G) {
+  uint32_t best = uint32_t(nblk) | (1u << 8);
   int best_cost = (tiles + G - 1) / G * nblk;
-  if (tiles > kMaxTileCounters) return best;
-  for (int sl = 2; sl <= planned; ++sl) {
-    const int b = (nblk + sl - 1) / sl;
-    const int items = tiles * ((nblk + b - 1) / b);
-    const int cost = (items + G - 1) / G * (b + kFinishStages);
+  for (int sl = 2; sl <= planned && tiles <= kMaxTileCounters; ++sl) {
+    const int b = (nblk + sl - 1) / sl, ns = (nblk + b - 1) / b;
+    const int cost = (tiles * ns + G - 1) / G * (b + kFinishStages);
     if (cost < best_cost) {
       best_cost = cost;
-      best = b;
+      best = uint32_t(b) | uint32_t(ns) << 8;
+    }
+  }
+  const int whole = tiles / G * G, rest = tiles - whole;
+  for (int sl = 2; sl <= planned && whole > 0 && rest > 0; ++sl) {
+    const int b = (nblk + sl - 1) / sl, ns = (nblk + b - 1) / b;
+    if (rest * ns > G) break;
+    const int cost = whole / G * nblk + b + kFinishStages;
+    if (cost < best_cost) {
+      best_cost = cost;
+      best = uint32_t(b) | uint32_t(ns) << 8 | kUpMixed;
     }
   }
   return best;
@@ -311,7 +326,8 @@ struct Params {
   const uint16_t *x;          // [B, d]
   const uint16_t *W[3];       // G, U: [E, d, I]; D: [E, I, d]
   int B, d, E, I, k;
-  int slices, slice_rows;     // gate/up reduction slices over d (1: whole of d, h formed in the epilogue)
+  int slices;                 // most gate/up d slices (the partial sums the workspace holds)
+  int n_ustrips;              // 64-column strips of I
   int P;                      // B * k
   float *gpart;               // [slices][2][P][I] gate/up partial sums by pair
   uint16_t *h;                // [P][I] SiLU(g) * u by pair
@@ -327,14 +343,24 @@ struct Params {
   uint32_t *grp_cnt;          // per (strip, token group): slots counted, one 128-byte line each
   uint32_t *tile_cnt;         // per gate/up tile (sliced path): d slices counted
   int n_dstrips;              // 128-column strips of d
-  int dslices, dslice_rows;   // down reduction (I) slices (1: all of I)
+  int dslices;                // most down I slices (the partial rows the workspace holds)
+};
+
+// The work split of one launch, chosen on the device from the active-expert
+// count (Params stays as the launch passed it).
+struct Split {
+  int slices, slice_rows;    // gate/up: d slices of a split tile, rows per slice
+  int up_whole;              // gate/up tiles taken whole (the first ones; h formed in the epilogue)
+  int dslices, dslice_rows;  // down: I slices of an item (1: all of I), rows per slice
 };
 
 // By active-expert count: gate/up stages of kBK rows per d slice (all of d
 // for whole tiles). A kernel argument of its own, never written, so that the
 // kernel reads the entry it needs from the argument segment.
 struct UpPlan {
-  uint32_t e2[(kMaxE + 2) / 2];  // entry n in half n % 2 of word n / 2: stages per slice | slices << 8
+  // Entry n in half n % 2 of word n / 2: stages per slice | slices << 8 |
+  // kUpMixed (the tiles of whole rounds of the grid are taken whole).
+  uint32_t e2[(kMaxE + 2) / 2];
 };
 
 // A position in a workgroup's stage sequence. The workgroup's items are
@@ -344,7 +370,7 @@ struct UpPlan {
 // tiles of D) and the A tile of the same reduction rows (x rows gathered by
 // token, or h rows by pair). All fields are wave-uniform.
 struct Cursor {
-  int item, n_items, n_up, per_up, per_dn;
+  int item, n_items, n_up, per_dn;
   int e, p0, T, strip, ks, row0, nrows, nst, npass, pass, kst;
   bool valid, up;
 };
@@ -353,6 +379,7 @@ template <int MTX>
 struct Stream {
   using S = Shape<2, MTX>;
   const Params &p;
+  const Split sp;
   uint32_t meta;            // LDS address of the routing lists
   int wave, lane, g, j;
   uint32_t wv_up[4];        // weight copy offsets within a stage (row stride I)
@@ -360,7 +387,8 @@ struct Stream {
   uint32_t trc[2];          // transposing-read offsets within a weight tile
   uint32_t xrd;             // A-fragment read offset within a k-step sub-tile
 
-  __device__ __forceinline__ Stream(const Params &pp, uint32_t meta_addr) : p(pp), meta(meta_addr) {
+  __device__ __forceinline__ Stream(const Params &pp, const Split &s, uint32_t meta_addr)
+      : p(pp), sp(s), meta(meta_addr) {
     wave = wave_id();
     lane = threadIdx.x & 63;
     g = lane >> 4;
@@ -385,23 +413,41 @@ struct Stream {
     c.valid = c.item < c.n_items;
     if (!c.valid) return;
     c.up = c.item < c.n_up;
-    int a;
+    // The fields are computed in locals and stored once below (stores of
+    // different fields in the two branches were merged through a pointer
+    // phi, which kept the cursor in scratch memory).
+    int a, strip, ks, row0, nrows;
     if (c.up) {
-      a = c.item / c.per_up;
-      const int rem = c.item - a * c.per_up;
-      c.strip = rem / p.slices;
-      c.ks = rem - c.strip * p.slices;
-      c.row0 = c.ks * p.slice_rows;
-      c.nrows = min(p.slice_rows, p.d - c.row0);
+      // Whole tiles first (ks = -1), then the d slices of each split tile.
+      int tile;
+      if (c.item < sp.up_whole) {
+        tile = c.item;
+        ks = -1;
+        row0 = 0;
+        nrows = p.d;
+      } else {
+        const int j = c.item - sp.up_whole;
+        const int ts = j / sp.slices;
+        tile = sp.up_whole + ts;
+        ks = j - ts * sp.slices;
+        row0 = ks * sp.slice_rows;
+        nrows = min(sp.slice_rows, p.d - row0);
+      }
+      a = tile / p.n_ustrips;
+      strip = tile - a * p.n_ustrips;
     } else {
       const int jd = c.item - c.n_up;
       a = jd / c.per_dn;
       const int rem = jd - a * c.per_dn;
-      c.strip = rem / p.dslices;
-      c.ks = rem - c.strip * p.dslices;
-      c.row0 = c.ks * p.dslice_rows;
-      c.nrows = min(p.dslice_rows, p.I - c.row0);
+      strip = rem / sp.dslices;
+      ks = rem - strip * sp.dslices;
+      row0 = ks * sp.dslice_rows;
+      nrows = min(sp.dslice_rows, p.I - row0);
     }
+    c.strip = strip;
+    c.ks = ks;
+    c.row0 = row0;
+    c.nrows = nrows;
     c.e = __builtin_amdgcn_readfirstlane(lds_i16(meta + kMetaAct + 2 * a));
     c.p0 = __builtin_amdgcn_readfirstlane(lds_i16(meta + kMetaOff + 2 * a));
     c.T = __builtin_amdgcn_readfirstlane(lds_i16(meta + kMetaOff + 2 * a + 2)) - c.p0;
@@ -658,7 +704,7 @@ __device__ __forceinline__ void epilogue(const Cursor &c, const Params &p, uint3
   const int g = lane >> 4, j = lane & 15;
   const int T = min(kMaxTok, c.T - c.pass * kMaxTok);
   const int pbase = c.p0 + c.pass * kMaxTok;
-  if (UP && p.slices == 1) {
+  if (UP && c.ks < 0) {
     // The whole reduction is in the accumulators: h = SiLU(g) * u by pair.
     const int col = c.strip * kStripCols + 16 * wave + j;
     if (col < p.I) {
@@ -712,32 +758,33 @@ __device__ __forceinline__ void epilogue(const Cursor &c, const Params &p, uint3
 // the counter back to zero. So h is complete once every workgroup has
 // finished its gate/up items, and one grid barrier separates gate/up from
 // down. `flag` is an int in LDS.
-__device__ __forceinline__ void finish_up(const Cursor &c, const Params &p, int *flag) {
+__device__ __forceinline__ void finish_up(const Cursor &c, const Params &p, const Split &sp, int *flag) {
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   if (threadIdx.x == 0) {
-    uint32_t *cnt = p.tile_cnt + size_t(c.item / p.slices) * kTileCntStride;
+    // Split tiles are counted in order: counter (item - up_whole) / slices.
+    uint32_t *cnt = p.tile_cnt + size_t((c.item - sp.up_whole) / sp.slices) * kTileCntStride;
     const uint32_t before = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const bool last = before + 1 == uint32_t(p.slices);
+    const bool last = before + 1 == uint32_t(sp.slices);
     if (last) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     *flag = last;
   }
   __syncthreads();
   if (!*flag) return;
   const uint32_t blk = uint32_t(p.P) * uint32_t(p.I) * 4u;  // bytes of one [P][I] block
-  const __amdgpu_buffer_rsrc_t r = make_rsrc(p.gpart, uint32_t(p.slices) * 2u * blk);
+  const __amdgpu_buffer_rsrc_t r = make_rsrc(p.gpart, uint32_t(sp.slices) * 2u * blk);
   const int col0 = c.strip * kStripCols;
   for (int u = threadIdx.x; u < c.T * (kStripCols / 4); u += kThreads) {
     const int m = u / (kStripCols / 4);
     const int col = col0 + (u - m * (kStripCols / 4)) * 4;  // I % 8 == 0: col < I means col + 3 < I
     if (col >= p.I) continue;
     const uint32_t off = (uint32_t(c.p0 + m) * uint32_t(p.I) + uint32_t(col)) * 4u;
-    // Slices past p.slices load slice 0 again and are masked out: every
+    // Slices past sp.slices load slice 0 again and are masked out: every
     // load is unconditional and read at once (consume).
     float4 gv[kUpMaxSlices], uv[kUpMaxSlices];
 #pragma unroll
     for (int sl = 0; sl < kUpMaxSlices; ++sl) {
-      const uint32_t so = uint32_t(sl < p.slices ? sl : 0) * 2u * blk;
+      const uint32_t so = uint32_t(sl < sp.slices ? sl : 0) * 2u * blk;
       gv[sl] = ld_dev4(r, off + so);
       uv[sl] = ld_dev4(r, off + so + blk);
     }
@@ -749,7 +796,7 @@ __device__ __forceinline__ void finish_up(const Cursor &c, const Params &p, int 
     float4 g = make_float4(0, 0, 0, 0), v = make_float4(0, 0, 0, 0);
 #pragma unroll
     for (int sl = 0; sl < kUpMaxSlices; ++sl) {
-      const bool in = sl < p.slices;
+      const bool in = sl < sp.slices;
       const float4 a = in ? gv[sl] : make_float4(0, 0, 0, 0);
       const float4 b = in ? uv[sl] : make_float4(0, 0, 0, 0);
       g.x += a.x; g.y += a.y; g.z += a.z; g.w += a.w;
@@ -801,12 +848,11 @@ __device__ __forceinline__ float4 ld_part4(__amdgpu_buffer_rsrc_t r, uint32_t of
                           : __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, int(off), 0, kPolicyDevice));
   return make_float4(v[0], v[1], v[2], v[3]);
 }
-__device__ __forceinline__ void combine_group(const Params &p, const uint32_t *fill, int grp, int strip,
-                                              bool local) {
+__device__ __forceinline__ void combine_group(const Params &p, int ds, const uint32_t *fill, int grp,
+                                              int strip, bool local) {
   const int t = grp * kTokGroup + (threadIdx.x >> 4);
   const int col = strip * 2 * kStripCols + (threadIdx.x & 15) * 8;
   if (t >= p.B || col >= p.d) return;
-  const int ds = p.dslices;
   const int nf = int(fill[t]);
   const int per_round = max(1, 8 / ds);  // slots per round
   const __amdgpu_buffer_rsrc_t rp = make_rsrc(p.part, uint32_t(ds) * uint32_t(p.P) * uint32_t(p.d) * 4u);
@@ -882,8 +928,8 @@ __device__ __forceinline__ void combine_group(const Params &p, const uint32_t *f
 // (combine_group) and resets the counter. A count is taken only after this
 // workgroup's stores have completed, so the last one finds every row of the
 // group in place.
-__device__ __forceinline__ void finish_down(const Cursor &c, const Params &p, unsigned char *meta,
-                                            int wave, int lane) {
+__device__ __forceinline__ void finish_down(const Cursor &c, const Params &p, const Split &sp,
+                                            unsigned char *meta, int wave, int lane) {
   const int T = min(kMaxTok, c.T - c.pass * kMaxTok);
   const int pbase = c.p0 + c.pass * kMaxTok;
   int32_t *last = reinterpret_cast<int32_t *>(meta + kMetaLast);
@@ -910,7 +956,7 @@ __device__ __forceinline__ void finish_down(const Cursor &c, const Params &p, un
       const uint64_t now = __hip_atomic_fetch_add(group_counter(p, grp, c.strip), add,
                                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + add;
       const uint64_t s0 = now & 0xFFFFu, s1 = (now >> 16) & 0xFFFFu, s2 = now >> 32;
-      mine = s0 == gfill[grp] * uint32_t(p.dslices);
+      mine = s0 == gfill[grp] * uint32_t(sp.dslices);
       local = mine && s1 * s1 == s0 * s2 && s1 == s0 * x;
     }
     const unsigned long long b = __ballot(mine);
@@ -922,7 +968,8 @@ __device__ __forceinline__ void finish_down(const Cursor &c, const Params &p, un
   const int n = *n_last;
   for (int q = 0; q < n; ++q) {
     const int grp = last[q] & 0xFFFF;
-    combine_group(p, reinterpret_cast<const uint32_t *>(meta + kMetaFill), grp, c.strip, (last[q] >> 16) != 0);
+    combine_group(p, sp.dslices, reinterpret_cast<const uint32_t *>(meta + kMetaFill), grp, c.strip,
+                  (last[q] >> 16) != 0);
     if (threadIdx.x == 0)
       __hip_atomic_store(group_counter(p, grp, c.strip), uint64_t(0), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
@@ -1071,25 +1118,29 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_kernel(Params p, const UpPlan
 
   // The gate/up split for this many active experts, chosen on the host
   // (plan_gate_up): stages of kBK rows per d slice, all of d for whole tiles.
+  const int up_tiles = nact * p.n_ustrips;
+  Split sp;
   if constexpr (MTX < 4) {
     const uint32_t e = (up.e2[nact >> 1] >> (16 * (nact & 1))) & 0xFFFFu;
-    p.slices = int(e >> 8);
-    p.slice_rows = p.slices == 1 ? p.d : int(e & 0xFFu) * kBK;
+    sp.slices = int((e >> 8) & 0x7Fu);
+    sp.slice_rows = int(e & 0xFFu) * kBK;
+    sp.up_whole = sp.slices == 1 ? up_tiles : (e & kUpMixed) ? up_tiles / int(gridDim.x) * int(gridDim.x) : 0;
   } else {
     // 64-token passes: decided here, by a simpler rule (reading the table,
-    // or running split_stages here, slowed this instantiation's stage loop
+    // or running plan_split here, slowed this instantiation's stage loop
     // by 2-6%): as many of the planned slices as leave every item a
     // workgroup of its own, else whole d.
-    const int up_tiles = nact * ((p.I + kStripCols - 1) / kStripCols);
     const int nblk = (p.d + kBK - 1) / kBK;
     const int sl = min(p.slices, int(gridDim.x) / max(up_tiles, 1));
     if (sl <= 1 || up_tiles > kMaxTileCounters) {
-      p.slices = 1;
-      p.slice_rows = p.d;
+      sp.slices = 1;
+      sp.slice_rows = p.d;
+      sp.up_whole = up_tiles;
     } else {
       const int blk = (nblk + sl - 1) / sl;
-      p.slices = (nblk + blk - 1) / blk;
-      p.slice_rows = blk * kBK;
+      sp.slices = (nblk + blk - 1) / blk;
+      sp.slice_rows = blk * kBK;
+      sp.up_whole = 0;
     }
   }
   // The down split: as many I slices, up to the planned number (whose
@@ -1099,15 +1150,14 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_kernel(Params p, const UpPlan
     const int nbi = (p.I + kBK - 1) / kBK;
     const int ds = max(1, min(p.dslices, int(gridDim.x) / max(nact * p.n_dstrips, 1)));
     const int blk = (nbi + ds - 1) / ds;
-    p.dslices = (nbi + blk - 1) / blk;
-    p.dslice_rows = blk * kBK;
+    sp.dslices = (nbi + blk - 1) / blk;
+    sp.dslice_rows = blk * kBK;
   }
 
-  const Stream<MTX> st(p, lds_addr(meta));
+  const Stream<MTX> st(p, sp, lds_addr(meta));
   Cursor cons;
-  cons.per_up = ((p.I + kStripCols - 1) / kStripCols) * p.slices;
-  cons.per_dn = p.n_dstrips * p.dslices;
-  cons.n_up = nact * cons.per_up;
+  cons.per_dn = p.n_dstrips * sp.dslices;
+  cons.n_up = sp.up_whole + (up_tiles - sp.up_whole) * sp.slices;
   cons.n_items = cons.n_up + nact * cons.per_dn;
   cons.item = blockIdx.x;
   st.decode(cons);
@@ -1131,7 +1181,7 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_kernel(Params p, const UpPlan
   // is then past stage s-1, so its slot takes stage s+kD, whose copies are
   // issued in two halves during the compute of stage s. The gate/up and down
   // phases run in loops of their own (UP), each with only its own code.
-  auto stage = [&](int s, auto up_tag) {
+  auto stage = [&](int s, auto up_tag) __attribute__((always_inline)) {
     constexpr bool UP = decltype(up_tag)::value;
     const int newer = issued - s - 1;
     switch (newer < kD - 1 ? newer : kD - 1) {
@@ -1157,10 +1207,10 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_kernel(Params p, const UpPlan
       epilogue<MTX, UP>(cons, p, st.meta, st.wave, st.lane, acc);
       clear(acc);
       if constexpr (UP) {
-        if (p.slices > 1 && (cons.pass + 1) * kMaxTok >= cons.T)
-          finish_up(cons, p, reinterpret_cast<int *>(meta + kMetaNLast));
+        if (cons.ks >= 0 && (cons.pass + 1) * kMaxTok >= cons.T)
+          finish_up(cons, p, sp, reinterpret_cast<int *>(meta + kMetaNLast));
       } else {
-        finish_down(cons, p, meta, st.wave, st.lane);
+        finish_down(cons, p, sp, meta, st.wave, st.lane);
       }
     }
     st.advance(cons);
@@ -1318,7 +1368,7 @@ void device_limits(int &cus, int &resident) {
   resident = per_cu * cus;
 }
 
-// Gate/up split (split_stages) for every possible active-expert count n (the
+// Gate/up split (plan_split) for every possible active-expert count n (the
 // count is only known on the device).
 static_assert(kMaxDim / kBK <= 255, "stages per slice fit a byte");
 void plan_gate_up(const Params &p, int G, UpPlan &up) {
@@ -1326,11 +1376,7 @@ void plan_gate_up(const Params &p, int G, UpPlan &up) {
   const int nblk = ceil_div(p.d, kBK);
   const int strips = ceil_div(p.I, kStripCols);
   const int planned = p.slices;
-  for (int n = 0; n <= p.E; ++n) {
-    const int blk = split_stages(n * strips, nblk, planned, G);
-    const int slices = ceil_div(nblk, blk);
-    up.e2[n >> 1] |= (uint32_t(blk) | uint32_t(slices) << 8) << (16 * (n & 1));
-  }
+  for (int n = 0; n <= p.E; ++n) up.e2[n >> 1] |= plan_split(n * strips, nblk, planned, G) << (16 * (n & 1));
 }
 
 // One workgroup per CU at most (grid = min(items, CUs)), so that the whole
@@ -1397,7 +1443,6 @@ hipError_t launch_expert_ffn(const void *x, const void *w_gate, const void *w_up
     p.I = I;
     p.k = k;
     p.slices = plan.up_slices;
-    p.slice_rows = plan.up_slice_rows;
     p.P = P;
     p.gpart = reinterpret_cast<float *>(ws + plan.up_part);
     p.h = reinterpret_cast<uint16_t *>(ws + plan.h);
@@ -1413,6 +1458,7 @@ hipError_t launch_expert_ffn(const void *x, const void *w_gate, const void *w_up
     p.grp_cnt = reinterpret_cast<uint32_t *>(ws + kGrpCntOffset);
     p.tile_cnt = reinterpret_cast<uint32_t *>(ws + kTileCntOffset);
     p.n_dstrips = ceil_div(d, 2 * kStripCols);
+    p.n_ustrips = ceil_div(I, kStripCols);
     p.dslices = plan.dn_slices;
     const int items = ffn_items(B, d, E, I, k, plan);
     // An expert has at most B tokens: A tiles of 16 * MTX rows cover them

@@ -1,5 +1,6 @@
 """The expert FFN's stage loop, as compiled for gfx950, holds no wait for
-vector memory that the compiler inserted itself.
+vector memory that the compiler inserted itself, and the kernel keeps no
+value in scratch memory.
 
 The stage loop keeps several stages of weight copies in flight and waits for
 them only through its own counted waits (blocks without MFMA). A wait that
@@ -9,6 +10,11 @@ only on some paths) would make every stage wait for the copies issued before
 it, and the stream would run at a fraction of its rate. This compiles
 ffn.hip to assembly with the product flags (no GPU needed) and checks every
 basic block of each ffn_kernel instantiation that issues MFMA.
+
+Scratch (private) memory is reached with vector memory instructions too, so
+a value kept there (a spill, or a variable the compiler could not keep in
+registers) makes the loop wait for the weight copies in flight wherever it
+is reloaded: every instantiation must have a private segment of 0 bytes.
 """
 import os
 import re
@@ -17,6 +23,13 @@ import subprocess
 import pytest
 
 from aware_expert_routing_amd import build as B
+
+
+@pytest.fixture(scope="module")
+def asm(tmp_path_factory):
+    if not os.path.exists("/opt/rocm/bin/hipcc"):
+        pytest.skip("hipcc not installed")
+    return _asm(tmp_path_factory.mktemp("isa"))
 
 
 def _asm(tmp_path, defines=()):
@@ -52,9 +65,18 @@ def _mfma_blocks_with_waits(asm):
     return found
 
 
-@pytest.mark.skipif(not os.path.exists("/opt/rocm/bin/hipcc"), reason="hipcc not installed")
-def test_stage_loop_has_no_compiler_inserted_memory_waits(tmp_path):
-    found = _mfma_blocks_with_waits(_asm(tmp_path))
+def test_stage_loop_has_no_compiler_inserted_memory_waits(asm):
+    found = _mfma_blocks_with_waits(asm)
     assert sorted(found) == [1, 2, 4], "every ffn_kernel instantiation is compiled"
     for mtx, bad in found.items():
         assert not bad, f"ffn_kernel<{mtx}>: vector-memory waits inside MFMA blocks: {bad}"
+
+
+def test_ffn_kernels_use_no_scratch(asm):
+    sizes = {}
+    for m in re.finditer(r"^\s*\.amdhsa_kernel (_ZN3moe\w*ffn_kernelILi(\d)E\w*)\s*$", asm, re.M):
+        end = asm.index(".end_amdhsa_kernel", m.end())
+        f = re.search(r"\.amdhsa_private_segment_fixed_size (\d+)", asm[m.end():end])
+        sizes[int(m.group(2))] = int(f.group(1))
+    assert sorted(sizes) == [1, 2, 4], sizes
+    assert all(v == 0 for v in sizes.values()), f"private segment bytes per lane: {sizes}"
