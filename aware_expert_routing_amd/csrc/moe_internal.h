@@ -90,30 +90,43 @@ inline Workspace plan_workspace(int B, int d, int E, int I, int k, moe_dtype_t d
   w.router_slices = ceil_div(d, kRouterRows);
   const size_t router_tiles = size_t(ceil_div(E, kRouterTile)) * ceil_div(B, kRouterTile);
   const size_t P = size_t(B) * size_t(k);
-  int slices = ceil_div(d, kUpSliceMin);
+  // Partial-sum regions: at least the minimum slice count's bytes, at least
+  // the budget when more slices fit it, so that a region never shrinks as B
+  // grows (a workspace sized for the largest call serves every smaller one).
   const size_t up_slice_bytes = 2 * P * size_t(I) * sizeof(float);
-  const int by_budget = int(kUpPartBudget / up_slice_bytes);
-  if (by_budget > slices) slices = by_budget < ceil_div(d, kStageRows) ? by_budget : ceil_div(d, kStageRows);
-  if (slices > kUpMaxSlices) slices = kUpMaxSlices;
+  int s_min = ceil_div(d, kUpSliceMin);
+  if (s_min > kUpMaxSlices) s_min = kUpMaxSlices;
+  int s_max = ceil_div(d, kStageRows);
+  if (s_max > kUpMaxSlices) s_max = kUpMaxSlices;
+  size_t up_bytes = size_t(s_max) * up_slice_bytes;
+  if (up_bytes > kUpPartBudget) up_bytes = kUpPartBudget;
+  if (up_bytes < size_t(s_min) * up_slice_bytes) up_bytes = size_t(s_min) * up_slice_bytes;
+  int slices = int(up_bytes / up_slice_bytes);
+  if (slices > s_max) slices = s_max;
+  if (slices < s_min) slices = s_min;
   int rows = ceil_div(d, slices);
   rows = ceil_div(rows, kStageRows) * kStageRows;
   w.up_slices = ceil_div(d, rows);
   w.up_slice_rows = rows;
   const size_t dn_slice_bytes = P * size_t(d) * sizeof(float);
-  int dn = int(kDnPartBudget / dn_slice_bytes);
-  if (dn > ceil_div(I, kStageRows)) dn = ceil_div(I, kStageRows);
-  if (dn > kDnMaxSlices) dn = kDnMaxSlices;
-  w.dn_slices = (dt == MOE_BF16 && dn > 1) ? dn : 1;
+  int ds_max = ceil_div(I, kStageRows);
+  if (ds_max > kDnMaxSlices) ds_max = kDnMaxSlices;
+  if (dt != MOE_BF16) ds_max = 1;
+  size_t dn_bytes = size_t(ds_max) * dn_slice_bytes;
+  if (dn_bytes > kDnPartBudget) dn_bytes = kDnPartBudget;
+  if (dn_bytes < dn_slice_bytes) dn_bytes = dn_slice_bytes;
+  w.dn_slices = int(dn_bytes / dn_slice_bytes);
+  if (w.dn_slices > ds_max) w.dn_slices = ds_max;
   const size_t esz = (dt == MOE_BF16) ? 2 : 4;
   size_t off = kCounterBytes;
   w.router_part = off;
   off = align256(off + router_tiles * w.router_slices * kRouterTile * kRouterTile * sizeof(float));
   w.up_part = off;
-  if (dt == MOE_BF16) off = align256(off + size_t(w.up_slices) * 2 * P * I * sizeof(float));
+  if (dt == MOE_BF16) off = align256(off + up_bytes);
   w.h = off;
   off = align256(off + P * I * esz);
   w.down_part = off;
-  off = align256(off + size_t(w.dn_slices) * P * size_t(d) * sizeof(float));
+  off = align256(off + dn_bytes);
   w.pair_of_slot = off;
   off = align256(off + P * sizeof(int32_t));
   w.total = off;

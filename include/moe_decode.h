@@ -105,8 +105,10 @@ typedef enum {
   MOE_ERR_SYNC_TIMEOUT = 6, /* from moe_workspace_check: a grid-wide wait of the bf16
                               expert FFN gave up in some call since the workspace was
                               zero-filled; those calls' outputs are unspecified        */
-  MOE_ERR_SCRATCH = 7      /* moe_layer_decode_static: the sizes need more scratch than
+  MOE_ERR_SCRATCH = 7,     /* moe_layer_decode_static: the sizes need more scratch than
                               its static array holds (MOE_STATIC_SCRATCH_BYTES)        */
+  MOE_STATUS_FORCE_32BIT = 0x7FFFFFFF /* not a status: makes every int32 value a valid
+                              moe_status_t, so that unknown codes are well defined  */
 } moe_status_t;
 
 /* Bytes at the start of a workspace that moe_workspace_check reads. */
@@ -115,7 +117,12 @@ typedef enum {
 /* Size of the static scratch of moe_layer_decode_static, per device. */
 #define MOE_STATIC_SCRATCH_BYTES (32u << 20)
 
-typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype_t;
+typedef enum {
+  MOE_F32 = 0,
+  MOE_BF16 = 1,
+  MOE_DTYPE_FORCE_32BIT = 0x7FFFFFFF /* not a dtype: every int32 value is a valid
+                                        moe_dtype_t (others are rejected)      */
+} moe_dtype_t;
 
 typedef enum {
   MOE_POLICY_TOPK = 0,   /* k experts per token (k <= E)                         */
