@@ -260,13 +260,10 @@ __device__ __forceinline__ void select_block(
   __shared__ int apos[kMaxE];
   __shared__ int aoff[kMaxE];
   __shared__ int s_n, s_total;
-  __shared__ float tok_mx[kMaxB], tok_sm[kMaxB], tok_thr[kMaxB];  // GREEDY per-token state
-  __shared__ int tok_cnt[kMaxB];
   __shared__ __attribute__((aligned(16))) uint32_t lscore[kMaxE];  // LYNX: expert scores
   __shared__ uint32_t lrank0[kWords];  // LYNX: rank-0 experts of the batch
-  __shared__ uint32_t w_best[kWaves];
-  __shared__ int w_e[kWaves];
-  __shared__ int s_pick;
+  __shared__ uint64_t w_pick[kWaves];  // GREEDY: each wave's best (gain, expert)
+  __shared__ int g_first[kMaxK];       // GREEDY: the first rounds' picks in order
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -475,11 +472,13 @@ __device__ __forceinline__ void select_block(
       if (keep) atomicOr(&allowed[tid >> 5], 1u << (tid & 31));
     }
   } else if (kind == MOE_POLICY_GREEDY) {
-    // Per-token softmax normalisers (probabilities are recomputed from the
-    // logits whenever needed, always by the same expression).
+    // Each token's probabilities, computed once from the logits.
+    float pr[TPW][NV];
 #pragma unroll
     for (int ti = 0; ti < TPW; ++ti) {
       const int t = wave + kWaves * ti;
+#pragma unroll
+      for (int v = 0; v < NV; ++v) pr[ti][v] = 0.0f;
       if (t < B) {
         float mx = -INFINITY;
 #pragma unroll
@@ -491,114 +490,112 @@ __device__ __forceinline__ void select_block(
         for (int v = 0; v < NV; ++v)
           if (lane + 64 * v < E) sm += expf(L[ti][v] - mx);
         sm = wave_sum(sm);
-        if (lane == 0) {
-          tok_mx[t] = mx;
-          tok_sm[t] = sm;
-          tok_thr[t] = 0.0f;
-          tok_cnt[t] = 0;
-        }
+#pragma unroll
+        for (int v = 0; v < NV; ++v)
+          if (lane + 64 * v < E) pr[ti][v] = expf(L[ti][v] - mx) / sm;
       }
     }
-    uint64_t kept = 0;  // bit ti*NV+v: expert lane+64v is among token slot ti's k largest in S
-    __syncthreads();
-    for (int r = 0; r < m; ++r) {
-      // Gains over this wave's tokens, then over the waves in order.
-      float g[NV];
+    // Token slot ti's k largest probabilities inside S, in descending order
+    // in lanes 0..k-1 (-1: no value yet), and its threshold thr (the k-th
+    // largest, 0 while S holds fewer than k experts). Wave-uniform thr.
+    float lst[TPW], thr[TPW];
 #pragma unroll
-      for (int v = 0; v < NV; ++v) g[v] = 0.0f;
-#pragma unroll
-      for (int ti = 0; ti < TPW; ++ti) {
-        const int t = wave + kWaves * ti;
-        if (t < B) {
-          const float mx = tok_mx[t], sm = tok_sm[t], thr = tok_thr[t];
-#pragma unroll
-          for (int v = 0; v < NV; ++v) g[v] += fmaxf(0.0f, expf(L[ti][v] - mx) / sm - thr);
-        }
-      }
-#pragma unroll
-      for (int v = 0; v < NV; ++v) {
-        const int e = lane + 64 * v;
-        if (e < E) psum[wave][e] = g[v];
-      }
-      __syncthreads();
-      if (wave * 64 < E) {
-        uint32_t key = 0;  // 0: not a candidate
-        if (tid < E && !bit_of(allowed, tid)) {
-          float gain = 0.0f;
-          for (int w = 0; w < kWaves; ++w) gain += psum[w][tid];
-          key = ord_bits(gain);
-        }
-        const uint32_t best = wave_max_u32(key);
-        const unsigned long long b = __ballot(key == best && key != 0);
-        if (lane == 0) {
-          w_best[wave] = best;
-          w_e[wave] = b ? wave * 64 + __builtin_ctzll(b) : -1;
-        }
-      }
-      __syncthreads();
-      if (tid == 0) {
-        uint32_t best = 0;
-        int e = -1;
-        for (int w = 0; w * 64 < E; ++w)
-          if (w_e[w] >= 0 && w_best[w] > best) {
-            best = w_best[w];
-            e = w_e[w];
-          }
-        s_pick = e;
-        if (e >= 0) allowed[e >> 5] |= 1u << (e & 31);
-      }
-      __syncthreads();
-      const int e = s_pick;
-      if (e < 0) break;  // block-uniform: no expert left
-      // Token slots update their k largest probabilities inside S.
+    for (int ti = 0; ti < TPW; ++ti) {
+      lst[ti] = -1.0f;
+      thr[ti] = 0.0f;
+    }
+    // Each token slot inserts its probability of expert e into its list; a
+    // value not above the k-th largest falls past lane k-1 and changes
+    // nothing.
+    auto insert = [&](int e) {
       const int ve = e >> 6, le = e & 63;
 #pragma unroll
       for (int ti = 0; ti < TPW; ++ti) {
-        const int t = wave + kWaves * ti;
-        if (t < B) {
-          const float mx = tok_mx[t], sm = tok_sm[t];
-          float pv[NV];
-#pragma unroll
-          for (int v = 0; v < NV; ++v) pv[v] = expf(L[ti][v] - mx) / sm;
-          float pe_l = 0.0f;
+        if (wave + kWaves * ti < B) {
+          float x = 0.0f;
 #pragma unroll
           for (int v = 0; v < NV; ++v)
-            if (v == ve) pe_l = pv[v];
-          const float pe = __shfl(pe_l, le);
-          int cnt = tok_cnt[t];
-          float thr = tok_thr[t];
-          bool changed = false;
-          if (cnt < k) {
-            if (lane == le) kept |= 1ull << (ti * NV + ve);
-            ++cnt;
-            changed = cnt == k;
-          } else if (pe > thr) {
-            // Drop one kept expert holding the threshold (the lowest index).
-            int drop = -1;
-#pragma unroll
-            for (int v = NV - 1; v >= 0; --v) {
-              const unsigned long long b =
-                  __ballot(((kept >> (ti * NV + v)) & 1ull) && pv[v] == thr);
-              if (b) drop = 64 * v + __builtin_ctzll(b);
-            }
-            if (lane == (drop & 63)) kept &= ~(1ull << (ti * NV + (drop >> 6)));
-            if (lane == le) kept |= 1ull << (ti * NV + ve);
-            changed = true;
-          }
-          if (changed) {
-            float mn = INFINITY;
-#pragma unroll
-            for (int v = 0; v < NV; ++v)
-              if ((kept >> (ti * NV + v)) & 1ull) mn = fminf(mn, pv[v]);
-            thr = wave_minf(mn);
-          }
-          if (lane == 0) {
-            tok_cnt[t] = cnt;
-            tok_thr[t] = thr;
-          }
+            if (v == ve) x = pr[ti][v];
+          const float pe = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(x), le));
+          // Lane j-1's entry (lane 0: +inf), row_shr:1 inside lanes 0..15.
+          const float prev = __uint_as_float(dpp<0x111, 0xF>(__float_as_uint(INFINITY), __float_as_uint(lst[ti])));
+          const float cur = lst[ti];
+          lst[ti] = cur >= pe ? cur : (prev >= pe ? pe : prev);
+          thr[ti] = fmaxf(0.0f, __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(lst[ti]), k - 1)));
         }
       }
+    };
+    bool taken = false;  // thread tid < E: expert tid is in S
+    // While S holds fewer than k experts every threshold is 0, so the first
+    // min(k, m) rounds all see the first round's gains: they take that
+    // round's largest gains in order (ties to the lower index) at once.
+    const int kk = min(k, m);
+    for (int r = 0; r < m; ++r) {
+      // Gains over this wave's token slots in order, then over the waves in
+      // order (by the threads tid < E, one expert each; waves without tokens
+      // add 0).
+      {
+        float g[NV];
+#pragma unroll
+        for (int v = 0; v < NV; ++v) g[v] = 0.0f;
+#pragma unroll
+        for (int ti = 0; ti < TPW; ++ti)
+          if (wave + kWaves * ti < B)
+#pragma unroll
+            for (int v = 0; v < NV; ++v) g[v] += fmaxf(0.0f, pr[ti][v] - thr[ti]);
+#pragma unroll
+        for (int v = 0; v < NV; ++v) {
+          const int e = lane + 64 * v;
+          if (e < E) psum[wave][e] = g[v];
+        }
+      }
+      __syncthreads();
+      uint32_t key = 0;  // thread tid < E: expert tid's gain (0: not a candidate)
+      if (tid < E && !taken) {
+        // All rows loaded before the first add (one LDS round trip).
+        float part[kWaves];
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) part[w] = psum[w][tid];
+        float gain = 0.0f;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) gain += part[w];
+        key = ord_bits(gain);
+      }
+      if (r == 0 && kk > 1) {
+        uint32_t *gkey = lscore;  // free outside LYNX
+        if (tid < E) gkey[tid] = key;
+        __syncthreads();
+        rank_keys_desc(gkey, E, krank);
+        __syncthreads();
+        if (tid < E && krank[tid] < kk) {
+          taken = true;
+          g_first[krank[tid]] = tid;
+        }
+        __syncthreads();
+        for (int j = 0; j < min(kk, E); ++j) insert(g_first[j]);
+        r = kk - 1;
+        continue;
+      }
+      if (wave * 64 < E) {
+        const uint32_t best = wave_max_u32(key);
+        const unsigned long long b = __ballot(key == best && key != 0);
+        // Larger gain first, then the lower index (complemented in the low word).
+        if (lane == 0)
+          w_pick[wave] = b ? (uint64_t(best) << 32) | uint32_t(~uint32_t(wave * 64 + __builtin_ctzll(b))) : 0ull;
+      }
+      __syncthreads();
+      uint64_t bp = 0;
+#pragma unroll
+      for (int w = 0; w < kMaxE / 64; ++w) {
+        const uint64_t q = w_pick[w];  // rows past E / 64 are never written
+        bp = (w * 64 < E && q > bp) ? q : bp;
+      }
+      if (bp == 0) break;  // block-uniform: no expert left
+      const int e = int(~uint32_t(bp));
+      if (tid == e) taken = true;
+      insert(e);
     }
+    if (tid < E && taken) atomicOr(&allowed[tid >> 5], 1u << (tid & 31));
   }
   __syncthreads();
 

@@ -259,7 +259,8 @@ def _sel_policies(E, k, B):
     out += [("oea", k0) for k0 in sorted({1, max(1, k // 2), k})]
     out += [("budget", m) for m in sorted({1, max(1, k - 1), max(1, E // 4), E})]
     if B * E <= 64 * 128:  # the oracle's greedy re-sorts per candidate: keep it small
-        out += [("greedy", m) for m in sorted({1, max(1, k - 1), max(1, E // 4)})]
+        out += [("greedy", m) for m in sorted({1, max(1, k - 1), max(1, E // 4)}
+                                              | ({E} if B * E <= 128 else set()))]
     mb = max(1, E // 2)
     out += [("hier", p) for p in sorted({(mb, max(1, min(mb, k // 2)), 2), (mb, min(mb, k + 2), 4),
                                           (E, max(1, k - 1), 1), (mb, max(1, mb // 2), B)})]
