@@ -262,7 +262,7 @@ __device__ __forceinline__ void select_block(
   __shared__ int s_n, s_total;
   __shared__ __attribute__((aligned(16))) uint32_t lscore[kMaxE];  // LYNX: expert scores
   __shared__ uint32_t lrank0[kWords];  // LYNX: rank-0 experts of the batch
-  __shared__ uint64_t w_pick[kWaves];  // GREEDY: each wave's best (gain, expert)
+  __shared__ unsigned long long g_best[2];  // GREEDY: each round's best (gain, expert)
   __shared__ int g_first[kMaxK];       // GREEDY: the first rounds' picks in order
 
   const int tid = threadIdx.x;
@@ -530,6 +530,9 @@ __device__ __forceinline__ void select_block(
     // min(k, m) rounds all see the first round's gains: they take that
     // round's largest gains in order (ties to the lower index) at once.
     const int kk = min(k, m);
+    // Round r's best (gain, expert) key, larger gain first, then the lower
+    // index (complemented in the low word); the two slots alternate.
+    if (tid == 0) g_best[0] = g_best[1] = 0ull;
     for (int r = 0; r < m; ++r) {
       // Gains over this wave's token slots in order, then over the waves in
       // order (by the threads tid < E, one expert each; waves without tokens
@@ -556,10 +559,12 @@ __device__ __forceinline__ void select_block(
         float part[kWaves];
 #pragma unroll
         for (int w = 0; w < kWaves; ++w) part[w] = psum[w][tid];
-        float gain = 0.0f;
+        // Pairwise, in a fixed tree.
 #pragma unroll
-        for (int w = 0; w < kWaves; ++w) gain += part[w];
-        key = ord_bits(gain);
+        for (int h = 1; h < kWaves; h *= 2)
+#pragma unroll
+          for (int w = 0; w < kWaves; w += 2 * h) part[w] += part[w + h];
+        key = ord_bits(part[0]);
       }
       if (r == 0 && kk > 1) {
         uint32_t *gkey = lscore;  // free outside LYNX
@@ -579,17 +584,14 @@ __device__ __forceinline__ void select_block(
       if (wave * 64 < E) {
         const uint32_t best = wave_max_u32(key);
         const unsigned long long b = __ballot(key == best && key != 0);
-        // Larger gain first, then the lower index (complemented in the low word).
-        if (lane == 0)
-          w_pick[wave] = b ? (uint64_t(best) << 32) | uint32_t(~uint32_t(wave * 64 + __builtin_ctzll(b))) : 0ull;
+        // A uniform value: one lane's atomic, no wave reduction around it.
+        const uint32_t lo = __builtin_amdgcn_readfirstlane(~uint32_t(wave * 64 + __builtin_ctzll(b)));
+        if (lane == 0 && b) atomicMax(&g_best[r & 1], (uint64_t(best) << 32) | lo);
       }
+      // The other slot was last read before this round's first barrier.
+      if (tid == 0) g_best[(r + 1) & 1] = 0ull;
       __syncthreads();
-      uint64_t bp = 0;
-#pragma unroll
-      for (int w = 0; w < kMaxE / 64; ++w) {
-        const uint64_t q = w_pick[w];  // rows past E / 64 are never written
-        bp = (w * 64 < E && q > bp) ? q : bp;
-      }
+      const uint64_t bp = g_best[r & 1];
       if (bp == 0) break;  // block-uniform: no expert left
       const int e = int(~uint32_t(bp));
       if (tid == e) taken = true;
