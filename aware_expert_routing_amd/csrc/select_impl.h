@@ -61,6 +61,9 @@ constexpr int kWaves = kThreads / 64;
 constexpr int kMaxTokPerWave = kMaxB / kWaves;  // token slots per wave at B = 256
 constexpr int kWords = kMaxE / 32;           // words of an expert bitmask
 constexpr int kTokWords = kMaxB / 32;        // words of a token bitmask
+constexpr int kGreedyTable = 8192;           // greedy: largest B * E held in LDS
+constexpr int kGreedyWaves = 4;              // greedy: waves running the rounds
+constexpr int kSpinLimit = 1 << 22;          // greedy: polls of the arrival count
 
 // Total order on float32 as unsigned integers; -0.0 maps like +0.0.
 __device__ __forceinline__ uint32_t ord_bits(float v) {
@@ -263,6 +266,8 @@ __device__ __forceinline__ void select_block(
   __shared__ __attribute__((aligned(16))) uint32_t lscore[kMaxE];  // LYNX: expert scores
   __shared__ uint32_t lrank0[kWords];  // LYNX: rank-0 experts of the batch
   __shared__ unsigned long long g_best[2];  // GREEDY: each round's best (gain, expert)
+  __shared__ float gP[TPW <= 4 ? kGreedyTable : 1];  // GREEDY: probabilities [B][E]
+  __shared__ int g_arrive;                  // GREEDY: arrivals of the four greedy waves
   __shared__ int g_first[kMaxK];       // GREEDY: the first rounds' picks in order
 
   const int tid = threadIdx.x;
@@ -495,109 +500,227 @@ __device__ __forceinline__ void select_block(
           if (lane + 64 * v < E) pr[ti][v] = expf(L[ti][v] - mx) / sm;
       }
     }
-    // Token slot ti's k largest probabilities inside S, in descending order
-    // in lanes 0..k-1 (-1: no value yet), and its threshold thr (the k-th
-    // largest, 0 while S holds fewer than k experts). Wave-uniform thr.
-    float lst[TPW], thr[TPW];
+    // Up to 64 tokens with the probability table in LDS: four waves run the
+    // rounds (the others wait at the barrier that ends this phase). Greedy
+    // wave gw holds the probabilities of tokens gw, gw + 4, gw + 8, ... in
+    // registers and the k largest of each inside S in one 16-lane row of a
+    // list register (descending in lanes 0..k-1, 0 where S holds fewer than
+    // k: the probabilities are >= 0, so lane k-1 is the threshold). Each
+    // round it adds its tokens' terms in order, meets the other three on an
+    // LDS arrival count (no workgroup barrier inside the rounds), adds the
+    // four partial gains in wave order and takes the same argmax as the
+    // others. While S holds fewer than k experts every threshold is 0, so
+    // the first min(k, m) rounds reuse the first round's gains.
+    const bool table = TPW <= 4 && B * E <= kGreedyTable;  // block-uniform
+    if constexpr (TPW <= 4) {
+      if (table) {
 #pragma unroll
-    for (int ti = 0; ti < TPW; ++ti) {
-      lst[ti] = -1.0f;
-      thr[ti] = 0.0f;
+        for (int ti = 0; ti < TPW; ++ti) {
+          const int t = wave + kWaves * ti;
+          if (t < B)
+#pragma unroll
+            for (int v = 0; v < NV; ++v)
+              if (lane + 64 * v < E) gP[t * E + lane + 64 * v] = pr[ti][v];
+        }
+        if (tid == 0) g_arrive = 0;
+        __syncthreads();
+        if (wave < kGreedyWaves) {
+          constexpr int kGT = kGreedyWaves * TPW;  // token slots of a greedy wave
+          const int gw = wave;
+          float P[kGT][NV];
+#pragma unroll
+          for (int i = 0; i < kGT; ++i) {
+            const int t = min(gw + kGreedyWaves * i, B - 1);
+#pragma unroll
+            for (int v = 0; v < NV; ++v) P[i][v] = gP[t * E + min(lane + 64 * v, E - 1)];
+          }
+          float lst[TPW];  // list register q: row r holds token slot 4q + r
+          float thr[kGT];
+#pragma unroll
+          for (int q = 0; q < TPW; ++q) lst[q] = 0.0f;
+#pragma unroll
+          for (int i = 0; i < kGT; ++i) thr[i] = 0.0f;
+          uint32_t key[NV], tk = 0;  // bit v of tk: expert lane + 64v is in S
+#pragma unroll
+          for (int v = 0; v < NV; ++v) key[v] = 0;
+          float *part = &psum[0][0];  // [2][kGreedyWaves][kMaxE], alternating
+          int rr = 0;                 // exchanges so far
+          const int kk = min(k, m);
+          for (int r = 0; r < m; ++r) {
+            if (r == 0 || r >= kk) {
+              float g[NV];
+#pragma unroll
+              for (int v = 0; v < NV; ++v) g[v] = 0.0f;
+#pragma unroll
+              for (int i = 0; i < kGT; ++i)
+                if (gw + kGreedyWaves * i < B)
+#pragma unroll
+                  for (int v = 0; v < NV; ++v) g[v] += fmaxf(0.0f, P[i][v] - thr[i]);
+              float *mine = part + ((rr & 1) * kGreedyWaves + gw) * kMaxE;
+#pragma unroll
+              for (int v = 0; v < NV; ++v)
+                if (lane + 64 * v < E) mine[lane + 64 * v] = g[v];
+              // Arrive after this wave's stores; wait for the other three
+              // (bounded: the four waves never wait on anything else).
+              if (lane == 0) __hip_atomic_fetch_add(&g_arrive, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+              const int target = kGreedyWaves * (rr + 1);
+              for (int it = 0; it < kSpinLimit; ++it)
+                if (__hip_atomic_load(&g_arrive, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) >= target) break;
+              const float *all = part + (rr & 1) * kGreedyWaves * kMaxE;
+#pragma unroll
+              for (int v = 0; v < NV; ++v) {
+                const int e = min(lane + 64 * v, E - 1);
+                float gain = all[e];
+#pragma unroll
+                for (int w = 1; w < kGreedyWaves; ++w) gain += all[w * kMaxE + e];
+                key[v] = lane + 64 * v < E ? ord_bits(gain) : 0u;
+              }
+              ++rr;
+            }
+            uint32_t best = 0;
+#pragma unroll
+            for (int v = 0; v < NV; ++v) {
+              const uint32_t kv = ((tk >> v) & 1u) ? 0u : key[v];
+              best = kv > best ? kv : best;
+            }
+            best = wave_max_u32(best);
+            if (best == 0) continue;  // no candidate left (m <= E: never)
+            int e = 0;
+#pragma unroll
+            for (int v = NV - 1; v >= 0; --v) {  // the lowest index holding `best` wins
+              const unsigned long long b = __ballot(!((tk >> v) & 1u) && key[v] == best);
+              if (b) e = 64 * v + __builtin_ctzll(b);
+            }
+            if ((e & 63) == lane) tk |= 1u << (e >> 6);
+            // Each token inserts its probability of e; a value not above the
+            // k-th largest falls past lane k-1 and changes nothing.
+#pragma unroll
+            for (int q = 0; q < TPW; ++q) {
+              if (gw + kGreedyWaves * 4 * q < B) {
+                const int t = min(gw + kGreedyWaves * (4 * q + (lane >> 4)), B - 1);
+                const float pe = gP[t * E + e];
+                const float cur = lst[q];
+                const float prev = __uint_as_float(dpp<0x111, 0xF>(__float_as_uint(INFINITY), __float_as_uint(cur)));
+                lst[q] = cur >= pe ? cur : (prev >= pe ? pe : prev);
+#pragma unroll
+                for (int row = 0; row < 4; ++row)
+                  thr[4 * q + row] = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(lst[q]), 16 * row + k - 1));
+              }
+            }
+          }
+          if (wave == 0) {
+#pragma unroll
+            for (int v = 0; v < NV; ++v)
+              if ((tk >> v) & 1u) atomicOr(&allowed[(lane + 64 * v) >> 5], 1u << ((lane + 64 * v) & 31));
+          }
+        }
+      }
     }
-    // Each token slot inserts its probability of expert e into its list; a
-    // value not above the k-th largest falls past lane k-1 and changes
-    // nothing.
-    auto insert = [&](int e) {
-      const int ve = e >> 6, le = e & 63;
+    if (!table) {
+      // Token slot ti's k largest probabilities inside S, in descending order
+      // in lanes 0..k-1 (-1: no value yet), and its threshold thr (the k-th
+      // largest, 0 while S holds fewer than k experts). Wave-uniform thr.
+      float lst[TPW], thr[TPW];
 #pragma unroll
       for (int ti = 0; ti < TPW; ++ti) {
-        if (wave + kWaves * ti < B) {
-          float x = 0.0f;
+        lst[ti] = -1.0f;
+        thr[ti] = 0.0f;
+      }
+      // Each token slot inserts its probability of expert e into its list; a
+      // value not above the k-th largest falls past lane k-1 and changes
+      // nothing.
+      auto insert = [&](int e) {
+        const int ve = e >> 6, le = e & 63;
 #pragma unroll
-          for (int v = 0; v < NV; ++v)
-            if (v == ve) x = pr[ti][v];
-          const float pe = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(x), le));
-          // Lane j-1's entry (lane 0: +inf), row_shr:1 inside lanes 0..15.
-          const float prev = __uint_as_float(dpp<0x111, 0xF>(__float_as_uint(INFINITY), __float_as_uint(lst[ti])));
-          const float cur = lst[ti];
-          lst[ti] = cur >= pe ? cur : (prev >= pe ? pe : prev);
-          thr[ti] = fmaxf(0.0f, __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(lst[ti]), k - 1)));
+        for (int ti = 0; ti < TPW; ++ti) {
+          if (wave + kWaves * ti < B) {
+            float x = 0.0f;
+#pragma unroll
+            for (int v = 0; v < NV; ++v)
+              if (v == ve) x = pr[ti][v];
+            const float pe = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(x), le));
+            // Lane j-1's entry (lane 0: +inf), row_shr:1 inside lanes 0..15.
+            const float prev = __uint_as_float(dpp<0x111, 0xF>(__float_as_uint(INFINITY), __float_as_uint(lst[ti])));
+            const float cur = lst[ti];
+            lst[ti] = cur >= pe ? cur : (prev >= pe ? pe : prev);
+            thr[ti] = fmaxf(0.0f, __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(lst[ti]), k - 1)));
+          }
         }
-      }
-    };
-    bool taken = false;  // thread tid < E: expert tid is in S
-    // While S holds fewer than k experts every threshold is 0, so the first
-    // min(k, m) rounds all see the first round's gains: they take that
-    // round's largest gains in order (ties to the lower index) at once.
-    const int kk = min(k, m);
-    // Round r's best (gain, expert) key, larger gain first, then the lower
-    // index (complemented in the low word); the two slots alternate.
-    if (tid == 0) g_best[0] = g_best[1] = 0ull;
-    for (int r = 0; r < m; ++r) {
-      // Gains over this wave's token slots in order, then over the waves in
-      // order (by the threads tid < E, one expert each; waves without tokens
-      // add 0).
-      {
-        float g[NV];
+      };
+      bool taken = false;  // thread tid < E: expert tid is in S
+      // While S holds fewer than k experts every threshold is 0, so the
+      // first min(k, m) rounds all see the first round's gains: they take
+      // that round's largest gains in order (ties to the lower index) at once.
+      const int kk = min(k, m);
+      // Round r's best (gain, expert) key, larger gain first, then the lower
+      // index (complemented in the low word); the two slots alternate.
+      if (tid == 0) g_best[0] = g_best[1] = 0ull;
+      for (int r = 0; r < m; ++r) {
+        // Gains over this wave's token slots in order, then over the waves in
+        // order (by the threads tid < E, one expert each; waves without tokens
+        // add 0).
+        {
+          float g[NV];
 #pragma unroll
-        for (int v = 0; v < NV; ++v) g[v] = 0.0f;
+          for (int v = 0; v < NV; ++v) g[v] = 0.0f;
 #pragma unroll
-        for (int ti = 0; ti < TPW; ++ti)
-          if (wave + kWaves * ti < B)
+          for (int ti = 0; ti < TPW; ++ti)
+            if (wave + kWaves * ti < B)
 #pragma unroll
-            for (int v = 0; v < NV; ++v) g[v] += fmaxf(0.0f, pr[ti][v] - thr[ti]);
+              for (int v = 0; v < NV; ++v) g[v] += fmaxf(0.0f, pr[ti][v] - thr[ti]);
 #pragma unroll
-        for (int v = 0; v < NV; ++v) {
-          const int e = lane + 64 * v;
-          if (e < E) psum[wave][e] = g[v];
-        }
-      }
-      __syncthreads();
-      uint32_t key = 0;  // thread tid < E: expert tid's gain (0: not a candidate)
-      if (tid < E && !taken) {
-        // All rows loaded before the first add (one LDS round trip).
-        float part[kWaves];
-#pragma unroll
-        for (int w = 0; w < kWaves; ++w) part[w] = psum[w][tid];
-        // Pairwise, in a fixed tree.
-#pragma unroll
-        for (int h = 1; h < kWaves; h *= 2)
-#pragma unroll
-          for (int w = 0; w < kWaves; w += 2 * h) part[w] += part[w + h];
-        key = ord_bits(part[0]);
-      }
-      if (r == 0 && kk > 1) {
-        uint32_t *gkey = lscore;  // free outside LYNX
-        if (tid < E) gkey[tid] = key;
-        __syncthreads();
-        rank_keys_desc(gkey, E, krank);
-        __syncthreads();
-        if (tid < E && krank[tid] < kk) {
-          taken = true;
-          g_first[krank[tid]] = tid;
+          for (int v = 0; v < NV; ++v) {
+            const int e = lane + 64 * v;
+            if (e < E) psum[wave][e] = g[v];
+          }
         }
         __syncthreads();
-        for (int j = 0; j < min(kk, E); ++j) insert(g_first[j]);
-        r = kk - 1;
-        continue;
+        uint32_t key = 0;  // thread tid < E: expert tid's gain (0: not a candidate)
+        if (tid < E && !taken) {
+          // All rows loaded before the first add (one LDS round trip).
+          float part[kWaves];
+#pragma unroll
+          for (int w = 0; w < kWaves; ++w) part[w] = psum[w][tid];
+          // Pairwise, in a fixed tree.
+#pragma unroll
+          for (int h = 1; h < kWaves; h *= 2)
+#pragma unroll
+            for (int w = 0; w < kWaves; w += 2 * h) part[w] += part[w + h];
+          key = ord_bits(part[0]);
+        }
+        if (r == 0 && kk > 1) {
+          uint32_t *gkey = lscore;  // free outside LYNX
+          if (tid < E) gkey[tid] = key;
+          __syncthreads();
+          rank_keys_desc(gkey, E, krank);
+          __syncthreads();
+          if (tid < E && krank[tid] < kk) {
+            taken = true;
+            g_first[krank[tid]] = tid;
+          }
+          __syncthreads();
+          for (int j = 0; j < min(kk, E); ++j) insert(g_first[j]);
+          r = kk - 1;
+          continue;
+        }
+        if (wave * 64 < E) {
+          const uint32_t best = wave_max_u32(key);
+          const unsigned long long b = __ballot(key == best && key != 0);
+          // A uniform value: one lane's atomic, no wave reduction around it.
+          const uint32_t lo = __builtin_amdgcn_readfirstlane(~uint32_t(wave * 64 + __builtin_ctzll(b)));
+          if (lane == 0 && b) atomicMax(&g_best[r & 1], (uint64_t(best) << 32) | lo);
+        }
+        // The other slot was last read before this round's first barrier.
+        if (tid == 0) g_best[(r + 1) & 1] = 0ull;
+        __syncthreads();
+        const uint64_t bp = g_best[r & 1];
+        if (bp == 0) break;  // block-uniform: no expert left
+        const int e = int(~uint32_t(bp));
+        if (tid == e) taken = true;
+        insert(e);
       }
-      if (wave * 64 < E) {
-        const uint32_t best = wave_max_u32(key);
-        const unsigned long long b = __ballot(key == best && key != 0);
-        // A uniform value: one lane's atomic, no wave reduction around it.
-        const uint32_t lo = __builtin_amdgcn_readfirstlane(~uint32_t(wave * 64 + __builtin_ctzll(b)));
-        if (lane == 0 && b) atomicMax(&g_best[r & 1], (uint64_t(best) << 32) | lo);
-      }
-      // The other slot was last read before this round's first barrier.
-      if (tid == 0) g_best[(r + 1) & 1] = 0ull;
-      __syncthreads();
-      const uint64_t bp = g_best[r & 1];
-      if (bp == 0) break;  // block-uniform: no expert left
-      const int e = int(~uint32_t(bp));
-      if (tid == e) taken = true;
-      insert(e);
+      if (tid < E && taken) atomicOr(&allowed[tid >> 5], 1u << (tid & 31));
     }
-    if (tid < E && taken) atomicOr(&allowed[tid >> 5], 1u << (tid & 31));
   }
   __syncthreads();
 

@@ -251,7 +251,7 @@ def test_route_select_ffn_equal_layer():
 # ------------------------------------------------------------- selection
 
 _SEL_SHAPES = [(1, 128, 8), (4, 16, 4), (3, 8, 8), (16, 64, 8), (16, 128, 8), (64, 128, 8),
-               (37, 100, 6), (256, 256, 16), (128, 64, 1)]
+               (37, 100, 6), (40, 256, 8), (256, 256, 16), (128, 64, 1)]
 
 
 def _sel_policies(E, k, B):
@@ -261,6 +261,8 @@ def _sel_policies(E, k, B):
     if B * E <= 64 * 128:  # the oracle's greedy re-sorts per candidate: keep it small
         out += [("greedy", m) for m in sorted({1, max(1, k - 1), max(1, E // 4)}
                                               | ({E} if B * E <= 128 else set()))]
+    elif B <= 64:  # probabilities too many for LDS: one round past the first k
+        out += [("greedy", k + 1)]
     mb = max(1, E // 2)
     out += [("hier", p) for p in sorted({(mb, max(1, min(mb, k // 2)), 2), (mb, min(mb, k + 2), 4),
                                           (E, max(1, k - 1), 1), (mb, max(1, mb // 2), B)})]
