@@ -51,6 +51,8 @@ def _parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--sweep", default=None,
                     help="run every configured (config, B, policy) case; one JSON line each to this file")
+    ap.add_argument("--sweep-policies", default=None, metavar="P1,P2",
+                    help="with --sweep: only these policies (e.g. greedy,hier)")
     ap.add_argument("--ffn-only", type=int, default=0, metavar="N",
                     help="run N eager moe_expert_ffn calls on rotating replicas and exit (for counter runs)")
     ap.add_argument("--read-ceiling", type=float, default=0.0, metavar="MB",
@@ -457,6 +459,9 @@ def main():
                     pols += [("hier", m // 4, m, 4) for m in cfg.budget_m]
                 if cname in ("qwen3_30b_bf16", "lynx_bf16"):
                     pols += [("lynx", 0, m, 0) for m in cfg.budget_m if m >= cfg.k]
+                if args.sweep_policies:
+                    keep = set(args.sweep_policies.split(","))
+                    pols = [p for p in pols if p[0] in keep]
                 for B in cfg.batches:
                     for pol, k0, m, g in pols:
                         rec = _run_case(cfg, B, pol, k0, m, inp, dev, args, with_cpu=False, g=g)
