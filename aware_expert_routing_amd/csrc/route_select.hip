@@ -26,6 +26,53 @@ struct SliceLogits {
   __device__ __forceinline__ float operator()(int t, int e) const {
     return router_logit(part, bias, t, e, tiles_e, slices);
   }
+  // The same sums as router_logit (bias, then slice 0, 1, ... in order) for
+  // every slot: the partial-tile loads of G slots x NV experts x 4 slices are
+  // all issued (indices clamped, no branch between them) before the first
+  // add, one round trip per 4 slices instead of one per logit.
+  template <int TPW, int NV>
+  __device__ __forceinline__ void gather(float (&L)[TPW][NV], int B, int wave, int lane) const {
+    constexpr int G = TPW < 8 / NV ? TPW : 8 / NV;  // slots per round trip
+    constexpr int S = 4;                            // slices per round trip
+    constexpr int kTile = kRtTile * kRtTile;
+#pragma unroll
+    for (int g0 = 0; g0 < TPW; g0 += G) {
+      if (g0 * kWaves >= B) break;  // block-uniform
+      float acc[G][NV];
+      const float *tp[G][NV];
+#pragma unroll
+      for (int i = 0; i < G; ++i)
+#pragma unroll
+        for (int v = 0; v < NV; ++v) {
+          const int t = min(wave + kWaves * (g0 + i), B - 1), e = min(lane + 64 * v, E - 1);
+          const int tile = e / kRtTile + tiles_e * (t / kRtTile);
+          tp[i][v] = part + size_t(tile) * slices * kTile + (t % kRtTile) * kRtTile + (e % kRtTile);
+          acc[i][v] = bias ? bias[e] : 0.0f;
+        }
+      for (int s0 = 0; s0 < slices; s0 += S) {
+        float p[G][NV][S];
+#pragma unroll
+        for (int i = 0; i < G; ++i)
+#pragma unroll
+          for (int v = 0; v < NV; ++v)
+#pragma unroll
+            for (int q = 0; q < S; ++q)
+              p[i][v][q] = __hip_atomic_load(const_cast<float *>(tp[i][v]) + min(s0 + q, slices - 1) * kTile,
+                                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+        for (int i = 0; i < G; ++i)
+#pragma unroll
+          for (int v = 0; v < NV; ++v)
+#pragma unroll
+            for (int q = 0; q < S; ++q)
+              if (s0 + q < slices) acc[i][v] += p[i][v][q];
+      }
+#pragma unroll
+      for (int i = 0; i < G; ++i)
+#pragma unroll
+        for (int v = 0; v < NV; ++v) L[g0 + i][v] = acc[i][v];
+    }
+  }
   __device__ __forceinline__ void emit(int t, int e, float v) const { out[size_t(t) * E + e] = v; }
 };
 

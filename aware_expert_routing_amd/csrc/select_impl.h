@@ -228,15 +228,25 @@ __device__ __forceinline__ void rank_keys_desc(const uint32_t *key, int E, int *
   if (r) atomicAdd(&rank[e], r);
 }
 
-// Source of the float32 logits: logit(t, e) with 0 <= t < B, 0 <= e < E,
-// and emit(t, e, v), called once for every (t, e) with the value read.
-// Logits stored in memory: device-scope loads (another workgroup of the same
-// kernel may have stored them); nothing to emit.
+// Source of the float32 logits: logit(t, e) with 0 <= t < B, 0 <= e < E;
+// gather(L, B, wave, lane), which fills L[ti][v] with logit(min(wave + 16ti,
+// B - 1), min(lane + 64v, E - 1)) for every slot, issuing the loads of
+// several slots before the first is used; and emit(t, e, v), called once for
+// every (t, e) with the value read. Logits stored in memory: device-scope
+// loads (another workgroup of the same kernel may have stored them); nothing
+// to emit.
 struct StoredLogits {
   const float *p;
   int E;
   __device__ __forceinline__ float operator()(int t, int e) const {
     return __hip_atomic_load(const_cast<float *>(p) + t * E + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  template <int TPW, int NV>
+  __device__ __forceinline__ void gather(float (&L)[TPW][NV], int B, int wave, int lane) const {
+#pragma unroll
+    for (int ti = 0; ti < TPW; ++ti)
+#pragma unroll
+      for (int v = 0; v < NV; ++v) L[ti][v] = (*this)(min(wave + kWaves * ti, B - 1), min(lane + 64 * v, E - 1));
   }
   __device__ __forceinline__ void emit(int, int, float) const {}
 };
@@ -295,18 +305,14 @@ __device__ __forceinline__ void select_block(
   // Phase 1: logits into registers. Indices are clamped so that every read
   // is in bounds; values outside [B, E) are never used as candidates.
   float L[TPW][NV];
+  src.template gather<TPW, NV>(L, B, wave, lane);
 #pragma unroll
   for (int ti = 0; ti < TPW; ++ti) {
-    if (ti * kWaves < B) {  // wave-uniform
-      const int tr = wave + kWaves * ti;
-      const int t = min(tr, B - 1);
+    const int t = wave + kWaves * ti;
+    if (t < B)
 #pragma unroll
-      for (int v = 0; v < NV; ++v) {
-        const int er = lane + 64 * v;
-        L[ti][v] = src(t, min(er, E - 1));
-        if (tr < B && er < E) src.emit(t, er, L[ti][v]);
-      }
-    }
+      for (int v = 0; v < NV; ++v)
+        if (lane + 64 * v < E) src.emit(t, lane + 64 * v, L[ti][v]);
   }
   __syncthreads();
 
