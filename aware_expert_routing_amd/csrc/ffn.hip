@@ -344,6 +344,7 @@ struct Params {
   uint32_t *tile_cnt;         // per gate/up tile (sliced path): d slices counted
   int n_dstrips;              // 128-column strips of d
   int dslices;                // most down I slices (the partial rows the workspace holds)
+  uint32_t *queue;            // B > 32: combine queue (pop, push, done words; entries)
 };
 
 // The work split of one launch, chosen on the device from the active-expert
@@ -920,14 +921,27 @@ __device__ __forceinline__ void combine_group(const Params &p, int ds, const uin
   *reinterpret_cast<uint4 *>(p.y + size_t(t) * p.d + col) = o;
 }
 
+// Combine queue words (Params::queue): pop index, push index, workgroups
+// done, each on a 128-byte line, then the entries (strip << 8 | group) + 1.
+constexpr int kQueuePop = 0;
+constexpr int kQueuePush = 32;
+constexpr int kQueueDone = 64;
+constexpr int kQueueEnt = 96;
+
 // End of a down pass (its rows stored by every wave). The pass adds, for
 // each 16-token group it has tokens of, their number to the group's counter
 // for the strip (one atomic per group, not per token: the atomics of one
 // counter are served in turn). The workgroup that brings a counter to the
-// group's number of filled slots forms y over the strip for the whole group
-// (combine_group) and resets the counter. A count is taken only after this
-// workgroup's stores have completed, so the last one finds every row of the
-// group in place.
+// group's number of filled slots resets it and forms y over the strip for
+// the group (combine_group), or, with more than 32 tokens (QUEUED: up to 16
+// groups per strip, which one workgroup would combine one round trip after
+// another), pushes the (strip, group) combine onto the queue that every
+// workgroup drains once its down items are done (drain_combines), so that a
+// strip's groups are combined by different workgroups at once (each then
+// waits one poll more; with two groups per strip that costs more than it
+// saves). A count is taken only after this workgroup's stores have
+// completed, so the last one finds every row of the group in place.
+template <bool QUEUED>
 __device__ __forceinline__ void finish_down(const Cursor &c, const Params &p, const Split &sp,
                                             unsigned char *meta, int wave, int lane) {
   const int T = min(kMaxTok, c.T - c.pass * kMaxTok);
@@ -960,8 +974,18 @@ __device__ __forceinline__ void finish_down(const Cursor &c, const Params &p, co
       local = mine && s1 * s1 == s0 * s2 && s1 == s0 * x;
     }
     const unsigned long long b = __ballot(mine);
-    if (mine) last[__builtin_amdgcn_mbcnt_hi(uint32_t(b >> 32), __builtin_amdgcn_mbcnt_lo(uint32_t(b), 0))] = grp | (local << 16);
-    if (lane == 0) *n_last = __popcll(b);
+    if constexpr (QUEUED) {
+      if (mine) {
+        __hip_atomic_store(group_counter(p, grp, c.strip), uint64_t(0), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const uint32_t i = __hip_atomic_fetch_add(p.queue + kQueuePush, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(p.queue + kQueueEnt + i, uint32_t((c.strip << 8 | grp) + 1), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+      }
+      if (lane == 0) *n_last = 0;
+    } else {
+      if (mine) last[__builtin_amdgcn_mbcnt_hi(uint32_t(b >> 32), __builtin_amdgcn_mbcnt_lo(uint32_t(b), 0))] = grp | (local << 16);
+      if (lane == 0) *n_last = __popcll(b);
+    }
   }
   __syncthreads();
   MOE_STAMP(8);
@@ -975,6 +999,61 @@ __device__ __forceinline__ void finish_down(const Cursor &c, const Params &p, co
   }
   __syncthreads();
   if (n) MOE_STAMP(9);
+}
+
+// The combine queue's consumer, run by every workgroup after its down items:
+// it takes entries in order (one atomic on the pop index each) until every
+// combine of the launch (128-column strips x token groups with a filled
+// slot) has been taken, waits for each taken entry to be pushed (bounded
+// polls; a wait that gives up sets the error word) and forms y for it. The
+// last workgroup done puts the queue's indices back to zero; each entry is
+// cleared by the workgroup that takes it.
+__device__ __forceinline__ void drain_combines(const Params &p, int ds, unsigned char *meta) {
+  const uint32_t *gfill = reinterpret_cast<const uint32_t *>(meta + kMetaGFill);
+  int32_t *code_lds = reinterpret_cast<int32_t *>(meta + kMetaLast);
+  int groups = 0;
+  for (int g = 0; g < (p.B + kTokGroup - 1) / kTokGroup; ++g) groups += gfill[g] != 0;
+  const uint32_t total = uint32_t(groups * p.n_dstrips);
+  bool combined = false;
+  for (;;) {
+    if (threadIdx.x == 0) {
+      int code = -1;
+      const uint32_t i = __hip_atomic_fetch_add(p.queue + kQueuePop, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (i < total) {
+        uint32_t v = 0;
+        for (uint32_t n = 0;
+             (v = __hip_atomic_load(p.queue + kQueueEnt + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) == 0;
+             ++n) {
+          if (n >= kSpinLimit) {
+            __hip_atomic_store(p.sync + kSyncErr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            break;
+          }
+          __builtin_amdgcn_s_sleep(1);
+        }
+        if (v) {
+          __hip_atomic_store(p.queue + kQueueEnt + i, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          code = int(v - 1);
+        }
+      }
+      *code_lds = code;
+    }
+    __syncthreads();
+    const int code = *code_lds;
+    __syncthreads();
+    if (code < 0) break;
+    combine_group(p, ds, reinterpret_cast<const uint32_t *>(meta + kMetaFill), code & 0xFF, code >> 8, false);
+    combined = true;
+  }
+  if (combined) MOE_STAMP(9);
+  if (threadIdx.x == 0) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this workgroup's queue accesses are done
+    if (__hip_atomic_fetch_add(p.queue + kQueueDone, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+        gridDim.x - 1) {
+      __hip_atomic_store(p.queue + kQueuePop, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(p.queue + kQueuePush, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(p.queue + kQueueDone, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
 }
 
 // y over the strips of token groups that have no filled slot at all (no
@@ -1210,7 +1289,7 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_kernel(Params p, const UpPlan
         if (cons.ks >= 0 && (cons.pass + 1) * kMaxTok >= cons.T)
           finish_up(cons, p, sp, reinterpret_cast<int *>(meta + kMetaNLast));
       } else {
-        finish_down(cons, p, sp, meta, st.wave, st.lane);
+        finish_down<(MTX == 4)>(cons, p, sp, meta, st.wave, st.lane);
       }
     }
     st.advance(cons);
@@ -1219,6 +1298,7 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_kernel(Params p, const UpPlan
   for (; cons.valid && cons.up; ++s) stage(s, std::true_type{});
   change_to_down<MTX>(p, st, prod, issued, s, stages, rel_base);
   for (; cons.valid; ++s) stage(s, std::false_type{});
+  if constexpr (MTX == 4) drain_combines(p, sp.dslices, meta);
   MOE_STAMP(10);
 }
 
@@ -1457,6 +1537,7 @@ hipError_t launch_expert_ffn(const void *x, const void *w_gate, const void *w_up
 #endif
     p.grp_cnt = reinterpret_cast<uint32_t *>(ws + kGrpCntOffset);
     p.tile_cnt = reinterpret_cast<uint32_t *>(ws + kTileCntOffset);
+    p.queue = reinterpret_cast<uint32_t *>(ws + kQueueOffset);
     p.n_dstrips = ceil_div(d, 2 * kStripCols);
     p.n_ustrips = ceil_div(I, kStripCols);
     p.dslices = plan.dn_slices;

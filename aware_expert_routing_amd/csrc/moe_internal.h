@@ -48,11 +48,11 @@ inline float lynx_bin_width(int E, int k) { return float(std::log(double(E) / do
 // share a workspace): the expert FFN's grid-barrier words (first 384 bytes),
 // the fused router + selection counter, the router's per-tile counters (up
 // to 256 tiles), the FFN's per-(16-token group, 128-column strip of d)
-// counters, each of those on a 128-byte line of its own, and the FFN's
-// per-gate/up-tile slice counters (atomics on one line
-// are served one after another). All are zero before the workspace's first
-// use. Every call leaves the counters at zero; the barrier's release word
-// only grows. No other step writes them.
+// counters, each of those on a 128-byte line of its own, the FFN's
+// per-gate/up-tile slice counters (atomics on one line are served one after
+// another) and the FFN's combine queue. All are zero before the workspace's
+// first use. Every call leaves the counters at zero; the barrier's release
+// word only grows. No other step writes them.
 constexpr size_t kSyncBytes = 2048;
 constexpr size_t kSyncErrOffset = 256;         // FFN: non-zero once a grid-barrier wait gave up
 static_assert(kSyncErrOffset + 4 <= MOE_WS_STATUS_BYTES, "status word inside the status bytes");
@@ -69,7 +69,13 @@ constexpr int kMaxTileCounters = 4096;
 constexpr int kTileCntStride = 16;                 // uint32 words between tile counters
 constexpr size_t kTileCntOffset =
     kGrpCntOffset + size_t(kMaxDim / (2 * kStripCols)) * kTokGroups * kCntStride * 4;
-constexpr size_t kCounterBytes = kTileCntOffset + size_t(kMaxTileCounters) * kTileCntStride * 4;
+// FFN, batches of more than 32 tokens: the combine queue. The pop index, the
+// push index and the count of workgroups done, each on a 128-byte line, then
+// one word per (128-column strip of d, token group) combine in push order
+// (0 until pushed).
+constexpr size_t kQueueOffset = kTileCntOffset + size_t(kMaxTileCounters) * kTileCntStride * 4;
+constexpr int kMaxCombines = (kMaxDim / (2 * kStripCols)) * kTokGroups;
+constexpr size_t kCounterBytes = kQueueOffset + 3 * 128 + size_t(kMaxCombines) * 4;
 
 // Workspace carve-up. Every segment starts on a 256-byte boundary.
 struct Workspace {

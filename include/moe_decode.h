@@ -170,8 +170,9 @@ typedef struct {
  * hipMemset after allocation); afterwards the caller must not write it. Its
  * first bytes hold the synchronisation words of the bf16 expert FFN (grid
  * barrier, a counter per output column strip and 16-token group, a counter
- * per gate/up tile when the gate/up product is split over d), which
- * every call leaves ready for the next one. The same workspace may serve
+ * per gate/up tile when the gate/up product is split over d, and, above 32
+ * tokens, a queue of (strip, group) combines that every workgroup drains),
+ * which every call leaves ready for the next one. The same workspace may serve
  * consecutive calls on one stream; calls that may overlap need separate
  * workspaces. The bf16 expert FFN runs one workgroup per compute unit and
  * needs all of them resident together: a device whose compute units cannot
