@@ -8,7 +8,10 @@
 // bf16 path: one persistent kernel, one workgroup per CU.
 //   * Work items: gate/up items (active expert x 64-column strip of I x slice
 //     of d) come first, then down items (active expert x 128-column strip of
-//     d x all of I); workgroup b takes items b, b+G, b+2G, ...
+//     d x slice of I); workgroup b takes items b, b+G, b+2G, ... The gate/up
+//     tiles are taken whole, split over d, or whole for the grid's full
+//     rounds and split for the rest (a plan costed per active-expert count on
+//     the host); down items are split over I when few experts are active.
 //   * Every item is a sequence of stages of kBK reduction rows; a stage holds
 //     two weight tiles (G and U, or two adjacent 64-column tiles of D) and the
 //     A tile of the same rows (x rows gathered by token, or h rows by pair).
@@ -22,12 +25,16 @@
 //     fragments along the reduction dimension are bank-conflict free.
 //   * An expert's tokens form the A operand: 16-row tiles of
 //     v_mfma_f32_16x16x32_bf16, up to 64 tokens per pass.
-//   * Gate/up slice partial sums go to the workspace; after a grid barrier
-//     the grid forms h = SiLU(g) * u; after a second one the down items run.
+//   * A whole gate/up tile writes h = SiLU(g) * u from its accumulators; the
+//     slices of a split tile store partial sums and the workgroup that counts
+//     a tile's last slice forms its h. One grid barrier then separates
+//     gate/up from down.
 //   * A down pass adds its tokens to per-(16-token group, strip) counters;
 //     the workgroup that completes a group's count forms y over that strip
-//     for the group's tokens, adding the slots in order (no float atomics:
-//     results are reproducible).
+//     for the group's tokens, adding the slots (and a slot's I slices) in
+//     order (no float atomics: results are reproducible). Above 32 tokens it
+//     queues the combine instead, and every workgroup drains the queue once
+//     its down items are done.
 // float32 path (small layers): plain dot products, 16 row groups per column.
 #include <atomic>
 #include <type_traits>
