@@ -11,7 +11,10 @@
 //     d x slice of I); workgroup b takes items b, b+G, b+2G, ... The gate/up
 //     tiles are taken whole, split over d, or whole for the grid's full
 //     rounds and split for the rest (a plan costed per active-expert count on
-//     the host); down items are split over I when few experts are active.
+//     the host); when whole tiles fit one round with workgroups to spare, the
+//     tiles of the slow strips (byte offset 384 mod 512 of a weight row) are
+//     split in two over d; down items are split over I when few experts are
+//     active.
 //   * Every item is a sequence of stages of kBK reduction rows; a stage holds
 //     two weight tiles (G and U, or two adjacent 64-column tiles of D) and the
 //     A tile of the same rows (x rows gathered by token, or h rows by pair).
@@ -360,6 +363,7 @@ struct Split {
   int slices, slice_rows;    // gate/up: d slices of a split tile, rows per slice
   int up_whole;              // gate/up tiles taken whole (the first ones; h formed in the epilogue)
   int dslices, dslice_rows;  // down: I slices of an item (1: all of I), rows per slice
+  int slow;                  // 1: strips 4q+3 split in two over d, the other strips whole
 };
 
 // By active-expert count: gate/up stages of kBK rows per d slice (all of d
@@ -441,8 +445,18 @@ struct Stream {
         row0 = ks * sp.slice_rows;
         nrows = min(sp.slice_rows, p.d - row0);
       }
-      a = tile / p.n_ustrips;
-      strip = tile - a * p.n_ustrips;
+      // Tile -> (expert, strip). Normally tile = expert * strips + strip.
+      // With sp.slow the whole tiles take, expert by expert, the strips
+      // other than 4q+3 (strip r + r/3 for the r-th of them) and the split
+      // tiles the strips 4q+3. Selects rather than branches: this code is
+      // inlined into the stage loop, whose scalar registers are scarce.
+      const int f = sp.slow, ns = p.n_ustrips >> 2;
+      const bool split = tile >= sp.up_whole;
+      const int u = f && split ? tile - sp.up_whole : tile;
+      const int dv = f ? (split ? ns : p.n_ustrips - ns) : p.n_ustrips;
+      a = u / dv;
+      const int r = u - a * dv;
+      strip = f ? (split ? 4 * r + 3 : r + r / 3) : r;
     } else {
       const int jd = c.item - c.n_up;
       a = jd / c.per_dn;
@@ -1147,9 +1161,12 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_kernel(Params p, const UpPlan
   // before the first value is used, so that the lists cost one round trip to
   // memory, not one per list, and no load or store sits behind a branch (the
   // compiler would sink the load into it): buffer loads past a list's end
-  // return zero, every LDS entry of the lists is written (entries past the
-  // active ones are never read), and the offsets' last rounds clamp to entry
-  // kMaxE, which all their lanes then write with the same value.
+  // return zero, the pair lists are loaded in as few rounds of 256 as cover
+  // the call's B*k pairs (the entries past them are never read; issuing the
+  // rounds for the largest batch every time put about 0.3 us of load
+  // instructions ahead of the first weight copies), and the offsets' last
+  // rounds clamp to entry kMaxE, which all their lanes then write with the
+  // same value.
   constexpr int kOffRounds = (kMaxE + 1 + kThreads - 1) / kThreads;
   constexpr int kActRounds = kMaxE / kThreads;
   constexpr int kPairRounds = kMaxPairs / kThreads;
@@ -1160,31 +1177,38 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_kernel(Params p, const UpPlan
   const __amdgpu_buffer_rsrc_t r_slot = make_rsrc(p.pair_slot, uint32_t(p.P) * 4u);
   const uint32_t rel_base = release_base(p.sync);
   const int nact = n_active[0];
-  int32_t offv[kOffRounds], actv[kActRounds], tokv[kPairRounds], slotv[kPairRounds];
+  int32_t offv[kOffRounds], actv[kActRounds];
 #pragma unroll
   for (int r = 0; r < kOffRounds; ++r)
     offv[r] = __builtin_amdgcn_raw_buffer_load_b32(r_off, min(int(threadIdx.x) + r * kThreads, kMaxE) * 4, 0, 0);
 #pragma unroll
   for (int r = 0; r < kActRounds; ++r)
     actv[r] = __builtin_amdgcn_raw_buffer_load_b32(r_act, (int(threadIdx.x) + r * kThreads) * 4, 0, 0);
+  auto lists = [&](auto rounds_tag) __attribute__((always_inline)) {
+    constexpr int R = decltype(rounds_tag)::value;
+    int32_t tokv[R], slotv[R];
 #pragma unroll
-  for (int r = 0; r < kPairRounds; ++r) {
-    const int o = (int(threadIdx.x) + r * kThreads) * 4;
-    tokv[r] = __builtin_amdgcn_raw_buffer_load_b32(r_tok, o, 0, 0);
-    slotv[r] = __builtin_amdgcn_raw_buffer_load_b32(r_slot, o, 0, 0);
-  }
+    for (int r = 0; r < R; ++r) {
+      const int o = (int(threadIdx.x) + r * kThreads) * 4;
+      tokv[r] = __builtin_amdgcn_raw_buffer_load_b32(r_tok, o, 0, 0);
+      slotv[r] = __builtin_amdgcn_raw_buffer_load_b32(r_slot, o, 0, 0);
+    }
 #pragma unroll
-  for (int r = 0; r < kOffRounds; ++r)
-    reinterpret_cast<int16_t *>(meta + kMetaOff)[min(int(threadIdx.x) + r * kThreads, kMaxE)] = int16_t(offv[r]);
+    for (int r = 0; r < kOffRounds; ++r)
+      reinterpret_cast<int16_t *>(meta + kMetaOff)[min(int(threadIdx.x) + r * kThreads, kMaxE)] = int16_t(offv[r]);
 #pragma unroll
-  for (int r = 0; r < kActRounds; ++r)
-    reinterpret_cast<int16_t *>(meta + kMetaAct)[threadIdx.x + r * kThreads] = int16_t(actv[r]);
+    for (int r = 0; r < kActRounds; ++r)
+      reinterpret_cast<int16_t *>(meta + kMetaAct)[threadIdx.x + r * kThreads] = int16_t(actv[r]);
 #pragma unroll
-  for (int r = 0; r < kPairRounds; ++r) {
-    const int i = int(threadIdx.x) + r * kThreads;
-    meta[kMetaTok + i] = uint8_t(tokv[r]);
-    reinterpret_cast<int16_t *>(meta + kMetaRow)[i] = int16_t(tokv[r] * p.k + slotv[r]);
-  }
+    for (int r = 0; r < R; ++r) {
+      const int i = int(threadIdx.x) + r * kThreads;
+      meta[kMetaTok + i] = uint8_t(tokv[r]);
+      reinterpret_cast<int16_t *>(meta + kMetaRow)[i] = int16_t(tokv[r] * p.k + slotv[r]);
+    }
+  };
+  if (p.P <= kThreads) lists(std::integral_constant<int, 1>{});
+  else if (p.P <= 4 * kThreads) lists(std::integral_constant<int, 4>{});
+  else lists(std::integral_constant<int, kPairRounds>{});
   uint32_t *fill = reinterpret_cast<uint32_t *>(meta + kMetaFill);
   for (int t = threadIdx.x; t < p.B; t += kThreads) fill[t] = 0;
   __syncthreads();
@@ -1211,6 +1235,23 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_kernel(Params p, const UpPlan
     sp.slices = int((e >> 8) & 0x7Fu);
     sp.slice_rows = int(e & 0xFFu) * kBK;
     sp.up_whole = sp.slices == 1 ? up_tiles : (e & kUpMixed) ? up_tiles / int(gridDim.x) * int(gridDim.x) : 0;
+    // Whole tiles in one round with workgroups to spare: the strips at byte
+    // offset 384 mod 512 of each weight row (strips 4q+3 when a row is a
+    // multiple of 512 bytes) stream about 20% slower than the others (per-
+    // strip stage stamps, on every XCD and in any item order), so their
+    // tiles set the end of gate/up. Those tiles are split in two d slices
+    // on workgroups that would otherwise wait (Qwen3-30B-shaped B=16
+    // oea(4): FFN 34.8 -> 33.6 us; B=8 oea(4) 33.5 -> 31.0; Qwen3-235B-
+    // shaped B=1 topk 63.5 -> 57.7).
+    sp.slow = 0;
+    const int nblk = (p.d + kBK - 1) / kBK;
+    if (sp.slices == 1 && (p.n_ustrips & 3) == 0 && (p.I * 2) % 512 == 0 && p.slices >= 2 && nblk >= 4 &&
+        up_tiles + nact * (p.n_ustrips >> 2) <= int(gridDim.x)) {
+      sp.slow = 1;
+      sp.slices = 2;
+      sp.slice_rows = (nblk + 1) / 2 * kBK;
+      sp.up_whole = nact * (p.n_ustrips - (p.n_ustrips >> 2));
+    }
   } else {
     // 64-token passes: decided here, by a simpler rule (reading the table,
     // or running plan_split here, slowed this instantiation's stage loop
@@ -1228,6 +1269,7 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_kernel(Params p, const UpPlan
       sp.slice_rows = blk * kBK;
       sp.up_whole = 0;
     }
+    sp.slow = 0;
   }
   // The down split: as many I slices, up to the planned number (whose
   // partial rows the workspace holds), as leave every down item a workgroup

@@ -341,6 +341,8 @@ def _custom_layer(B, d, E, I, k, dtype="bf16", seed=0, bias=None, wg_scale=1.0):
     (256, 64, 256, 64, 16, "hier", (96, 20, 8), "bf16"),  # 32 requests of 8 tokens
     (7, 136, 12, 40, 4, "hier", (9, 3, 3), "bf16"),      # ragged last request
     (9, 4096, 8, 64, 2, "topk", 0, "bf16"),      # deep reduction, several d slices
+    (6, 448, 8, 256, 2, "topk", 0, "bf16"),      # whole gate/up tiles but strip 3 split over d, ragged d
+    (16, 1024, 16, 512, 4, "oea", 2, "bf16"),    # the same with strips 3 and 7 of every expert split
 ])
 def test_edge_layers(B, d, E, I, k, policy, p, dtype):
     cfg, inp, dev = _custom_layer(B, d, E, I, k, dtype)
