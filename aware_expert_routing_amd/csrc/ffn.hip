@@ -2,8 +2,8 @@
 //   y[t] = sum_j w[t,j] * (SiLU(x_t G_e) * (x_t U_e)) D_e,  e = slot j's expert,
 // reading only the weights of experts in the active list ("Lynx", Technical
 // Summary 1: decode latency follows the number of distinct experts loaded;
-// "Opportunistic Expert Activation", abstract: MoE latency is governed by the
-// number of activated experts).
+// "Opportunistic Expert Activation", abstract: a decode step costs in
+// proportion to how many different experts the batch switches on).
 //
 // bf16 path: one persistent kernel, one workgroup per CU.
 //   * Work items: gate/up items (active expert x 64-column strip of I x slice
