@@ -542,7 +542,10 @@ def expert_ffn(x, ids, W, w_gate, w_up, w_down, dtype: str, tokens=None) -> np.n
     (when given) are left zero.
 
     Pinned by: one expert reduces to a dense SwiGLU from plain matmuls;
-    outputs are linear in D; experts no token selected do not matter.
+    outputs are linear in D; experts no token selected do not matter; and
+    each slot's weight multiplies its own expert's output (distinct experts
+    whose down matrices are distinct scales of one matrix, hand-worked and
+    over every policy), which a permutation of a token's weights fails.
     """
     X = widen(x, dtype)
     B, d = X.shape
