@@ -343,6 +343,7 @@ def _custom_layer(B, d, E, I, k, dtype="bf16", seed=0, bias=None, wg_scale=1.0):
     (9, 4096, 8, 64, 2, "topk", 0, "bf16"),      # deep reduction, several d slices
     (6, 448, 8, 256, 2, "topk", 0, "bf16"),      # whole gate/up tiles but strip 3 split over d, ragged d
     (16, 1024, 16, 512, 4, "oea", 2, "bf16"),    # the same with strips 3 and 7 of every expert split
+    (24, 1024, 16, 512, 4, "topk", 0, "bf16"),   # the same split in the 32-token instantiation
 ])
 def test_edge_layers(B, d, E, I, k, policy, p, dtype):
     cfg, inp, dev = _custom_layer(B, d, E, I, k, dtype)
