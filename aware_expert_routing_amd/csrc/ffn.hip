@@ -13,8 +13,8 @@
 //     rounds and split for the rest (a plan costed per active-expert count on
 //     the host); when whole tiles fit one round with workgroups to spare, the
 //     tiles of the slow strips (byte offset 384 mod 512 of a weight row) are
-//     split in two over d; down items are split over I when few experts are
-//     active.
+//     split in two over d, and in mixed plans they come last; down items are
+//     split over I when few experts are active.
 //   * Every item is a sequence of stages of kBK reduction rows; a stage holds
 //     two weight tiles (G and U, or two adjacent 64-column tiles of D) and the
 //     A tile of the same rows (x rows gathered by token, or h rows by pair).
@@ -363,7 +363,8 @@ struct Split {
   int slices, slice_rows;    // gate/up: d slices of a split tile, rows per slice
   int up_whole;              // gate/up tiles taken whole (the first ones; h formed in the epilogue)
   int dslices, dslice_rows;  // down: I slices of an item (1: all of I), rows per slice
-  int slow;                  // 1: strips 4q+3 split in two over d, the other strips whole
+  int slow;                  // 1: the tiles of strips 4q+3 come after the others' (below)
+  int nfast;                 // with slow: the tiles of the other strips, which come first
 };
 
 // By active-expert count: gate/up stages of kBK rows per d slice (all of d
@@ -446,13 +447,13 @@ struct Stream {
         nrows = min(sp.slice_rows, p.d - row0);
       }
       // Tile -> (expert, strip). Normally tile = expert * strips + strip.
-      // With sp.slow the whole tiles take, expert by expert, the strips
-      // other than 4q+3 (strip r + r/3 for the r-th of them) and the split
-      // tiles the strips 4q+3. Selects rather than branches: this code is
+      // With sp.slow the first sp.nfast tiles take, expert by expert, the
+      // strips other than 4q+3 (strip r + r/3 for the r-th of them) and the
+      // rest the strips 4q+3. Selects rather than branches: this code is
       // inlined into the stage loop, whose scalar registers are scarce.
       const int f = sp.slow, ns = p.n_ustrips >> 2;
-      const bool split = tile >= sp.up_whole;
-      const int u = f && split ? tile - sp.up_whole : tile;
+      const bool split = tile >= sp.nfast;
+      const int u = f && split ? tile - sp.nfast : tile;
       const int dv = f ? (split ? ns : p.n_ustrips - ns) : p.n_ustrips;
       a = u / dv;
       const int r = u - a * dv;
@@ -1245,13 +1246,21 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_kernel(Params p, const UpPlan
     // shaped B=1 topk 63.5 -> 57.7).
     sp.slow = 0;
     const int nblk = (p.d + kBK - 1) / kBK;
-    if (sp.slices == 1 && (p.n_ustrips & 3) == 0 && (p.I * 2) % 512 == 0 && p.slices >= 2 && nblk >= 4 &&
+    const bool strips4 = (p.n_ustrips & 3) == 0 && (p.I * 2) % 512 == 0;
+    if (sp.slices == 1 && strips4 && p.slices >= 2 && nblk >= 4 &&
         up_tiles + nact * (p.n_ustrips >> 2) <= int(gridDim.x)) {
       sp.slow = 1;
       sp.slices = 2;
       sp.slice_rows = (nblk + 1) / 2 * kBK;
       sp.up_whole = nact * (p.n_ustrips - (p.n_ustrips >> 2));
+    } else if (sp.slices > 1 && sp.up_whole > 0 && strips4) {
+      // Mixed plan: the slow strips' tiles last, so that the tiles split in
+      // the last round are mostly theirs and the workgroups that take a
+      // slice after a whole tile hold the other strips (Qwen3-30B-shaped
+      // B=32 oea(4) 59.2 -> 58.0 us, B=16 topk 59.8 -> 58.9).
+      sp.slow = 1;
     }
+    sp.nfast = sp.slow ? nact * (p.n_ustrips - (p.n_ustrips >> 2)) : sp.up_whole;
   } else {
     // 64-token passes: decided here, by a simpler rule (reading the table,
     // or running plan_split here, slowed this instantiation's stage loop
@@ -1270,6 +1279,7 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_kernel(Params p, const UpPlan
       sp.up_whole = 0;
     }
     sp.slow = 0;
+    sp.nfast = sp.up_whole;
   }
   // The down split: as many I slices, up to the planned number (whose
   // partial rows the workspace holds), as leave every down item a workgroup
