@@ -452,12 +452,12 @@ struct Stream {
       // rest the strips 4q+3. Selects rather than branches: this code is
       // inlined into the stage loop, whose scalar registers are scarce.
       const int f = sp.slow, ns = p.n_ustrips >> 2;
-      const bool split = tile >= sp.nfast;
-      const int u = f && split ? tile - sp.nfast : tile;
-      const int dv = f ? (split ? ns : p.n_ustrips - ns) : p.n_ustrips;
+      const bool slow_group = tile >= sp.nfast;
+      const int u = f && slow_group ? tile - sp.nfast : tile;
+      const int dv = f ? (slow_group ? ns : p.n_ustrips - ns) : p.n_ustrips;
       a = u / dv;
       const int r = u - a * dv;
-      strip = f ? (split ? 4 * r + 3 : r + r / 3) : r;
+      strip = f ? (slow_group ? 4 * r + 3 : r + r / 3) : r;
     } else {
       const int jd = c.item - c.n_up;
       a = jd / c.per_dn;
