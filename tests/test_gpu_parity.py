@@ -226,19 +226,21 @@ def test_workspace_shared_across_sizes():
         assert torch.equal(y, y_fresh), f"B={B} {pol}{p}"
 
 
-def test_route_select_ffn_equal_layer():
-    """The three standalone entry points reproduce the fused layer bit for bit."""
-    cfg = CONFIGS["lynx_bf16"]
-    inp, dev = _layer_inputs("lynx_bf16")
-    B = 16
-    Lg, rg, y = _run_layer(cfg, inp, dev, B, "budget", 0, 24)
+@pytest.mark.parametrize("cname,B,m", [("lynx_bf16", 16, 24), ("tiny_f32", 4, 8)])
+def test_route_select_ffn_equal_layer(cname, B, m):
+    """The three standalone entry points reproduce the fused layer bit for bit
+    (bf16: router and selection in one launch; float32: the same kernels)."""
+    cfg = CONFIGS[cname]
+    inp, dev = _layer_inputs(cname)
+    tdt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+    Lg, rg, y = _run_layer(cfg, inp, dev, B, "budget", 0, m)
     x = dev["x"][:B].contiguous()
-    ws = L.alloc_workspace(B, cfg.d, cfg.E, cfg.I, cfg.k, torch.bfloat16)
+    ws = L.alloc_workspace(B, cfg.d, cfg.E, cfg.I, cfg.k, tdt)
     lg = torch.empty((B, cfg.E), dtype=torch.float32, device="cuda")
     L.moe_route(x, dev["w_g"], dev["bias"], lg, ws)
     r = L.Routing(B, cfg.E, cfg.k)
-    L.moe_select(lg, L.make_policy("budget", cfg.k, 0, 24), r)
-    y2 = torch.empty((B, cfg.d), dtype=torch.bfloat16, device="cuda")
+    L.moe_select(lg, L.make_policy("budget", cfg.k, 0, m), r)
+    y2 = torch.empty((B, cfg.d), dtype=tdt, device="cuda")
     L.moe_expert_ffn(x, dev["w_gate"], dev["w_up"], dev["w_down"], r, y2, ws)
     torch.cuda.synchronize()
     assert np.array_equal(lg.cpu().numpy(), Lg)
